@@ -1,0 +1,328 @@
+"""Pins of the float64 oracle to things other than itself.
+
+Each test ties an oracle function to a closed form, an invariant or a brute-force
+computation fixed by the pages or by the mathematics:
+
+* Newton-Schulz: the iteration acts on singular values only, so for
+  M = U diag(sigma) V^T the result is U diag(f^5(sigma / ||M||_F)) V^T with
+  f(x) = a x + b x^3 + c x^5 ("Muon is Scalable for LLM Training", Sec. 2.1: Eq. 2
+  and the polynomial paragraph; the polar factor identity (M M^T)^(-1/2) M = U V^T
+  after Eq. 1). Checked against numpy's SVD, against exact rational arithmetic
+  on rank-1 inputs and against pure-Python scalar loops on diagonal inputs.
+* Lemma 1 (Sec. 2.2): update RMS law for full-rank matrices.
+* RowNorm: unit row / column norms and the RMS law they imply (reading R2).
+* Momentum (Eq. 1): geometric-series closed form.
+* Schedule: K = 1 is vanilla Muon; K = 3 gives one refresh in three steps, which
+  matches the pages' 28.62 -> 9.54 GiB and -66.7% communication figures.
+* A mutation check plants plausible mistakes in copies of the oracle and shows
+  that these pins reject each of them.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import muon_oracle as O
+from matrix_orthogonalising_optimizer_02_amd import workloads as WL
+
+HP = O.OracleHParams()
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_constants.json")
+
+
+def golden():
+    with open(GOLDEN) as fh:
+        return json.load(fh)
+
+
+def f_poly_composed(x, steps=5, a=HP.ns_a, b=HP.ns_b, c=HP.ns_c):
+    """f applied `steps` times to an array of singular values (the spectral closed form)."""
+    x = np.asarray(x, dtype=np.float64)
+    for _ in range(steps):
+        x = a * x + b * x ** 3 + c * x ** 5
+    return x
+
+
+def svd_closed_form(m, steps=5):
+    """U diag(f^steps(sigma/||M||_F)) V^T from LAPACK's SVD (thin)."""
+    m = np.asarray(m, dtype=np.float64)
+    u, s, vt = np.linalg.svd(m, full_matrices=False)
+    fro = math.sqrt(float(np.sum(s * s)))
+    return (u * f_poly_composed(s / fro, steps)) @ vt
+
+
+def rel_fro(x, ref):
+    den = np.linalg.norm(ref)
+    return np.linalg.norm(np.asarray(x) - np.asarray(ref)) / (den if den > 0 else 1.0)
+
+
+def gaussian(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ---------------------------------------------------------------- constants ----
+
+def test_defaults_are_the_pages_constants():
+    g = golden()
+    for field in ("ns_a", "ns_b", "ns_c", "ns_steps", "mu", "rms_scale", "period_k", "gamma"):
+        assert getattr(HP, field) == g[field]["value"], field
+
+
+def test_schedule_matches_pages_communication_ratio():
+    """One refresh in K steps: full-momentum traffic falls to 1/K (28.62 -> 9.54 GiB, -66.7%)."""
+    g = golden()
+    k = g["period_k"]["value"]
+    refresh = [s for s in range(12) if O.is_refresh_step(s, k)]
+    assert refresh == [0, 3, 6, 9]
+    frac = len(refresh) / 12
+    assert abs(g["comm_gib_vanilla_15b"]["value"] * frac - g["comm_gib_periodic_15b"]["value"]) < 0.005
+    assert abs(100 * (1 - frac) - g["comm_reduction_pct"]["value"]) < 0.05
+    # the top of the optimizer-time range is the 15B pair of figures
+    lo, hi = g["optimizer_time_reduction_pct_range"]["value"]
+    red = 100 * (1 - g["optimizer_time_15b_periodic"]["value"] / g["optimizer_time_15b_vanilla"]["value"])
+    assert abs(red - hi) < 0.05 and lo <= round(red, 1) <= hi
+
+
+# ------------------------------------------------------------ Newton-Schulz ----
+
+SHAPES = [(1, 7), (7, 1), (2, 2), (4, 4), (8, 32), (32, 8), (16, 16), (33, 77), (77, 33),
+          (128, 512), (512, 128), (64, 64)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_ns5_equals_svd_closed_form(shape):
+    m = gaussian(shape, hash(shape) % 2**31)
+    assert rel_fro(O.newton_schulz(m), svd_closed_form(m)) < 1e-10
+
+
+def test_ns5_single_128x512_workload_closed_form():
+    w, mp, g = WL.host_inputs(WL.SINGLE_128x512, 0)
+    m = O.momentum(mp, g, HP.mu)
+    assert rel_fro(O.newton_schulz(m), svd_closed_form(m)) < 1e-10
+
+
+def test_ns5_rank_one_exact_rational():
+    """Rank 1: X_0 = u v^T / (|u||v|) has the single singular value 1, so O = f^5(1) u^ v^T."""
+    a, b, c = (Fraction(str(HP.ns_a)), Fraction(str(HP.ns_b)), Fraction(str(HP.ns_c)))
+    x = Fraction(1)
+    iterates = []
+    for _ in range(5):
+        x = a * x + b * x ** 3 + c * x ** 5
+        iterates.append(float(x))
+    # first iterate is a + b + c exactly
+    assert iterates[0] == pytest.approx(0.701, abs=1e-15)
+    f5 = float(x)
+    assert abs(f5 - 0.696436) < 5e-7
+    rng = np.random.default_rng(7)
+    u, v = rng.standard_normal(24), rng.standard_normal(40)
+    m = np.outer(u, v) * 3.7
+    expect = f5 * np.outer(u / np.linalg.norm(u), v / np.linalg.norm(v))
+    assert np.max(np.abs(O.newton_schulz(m) - expect)) < 1e-12
+    # a single row is rank one: O = f^5(1) * v / |v|
+    row = rng.standard_normal((1, 9))
+    assert np.max(np.abs(O.newton_schulz(row) - f5 * row / np.linalg.norm(row))) < 1e-12
+
+
+def test_ns5_orthonormal_rows_scaled():
+    """Q with orthonormal rows scaled by c: all singular values c, normalised to 1/sqrt(m)."""
+    rng = np.random.default_rng(11)
+    q, _ = np.linalg.qr(rng.standard_normal((48, 12)))
+    q = q.T  # 12 x 48, orthonormal rows
+    expect = float(f_poly_composed(1 / math.sqrt(12))) * q
+    assert np.max(np.abs(O.newton_schulz(5.5 * q) - expect)) < 1e-12
+
+
+def test_ns5_diagonal_bruteforce_scalar_loops():
+    """Diagonal D: every iterate stays diagonal, each entry follows the scalar map alone."""
+    d = [0.9, -0.3, 0.05, 2.0]
+    nrm = math.sqrt(sum(x * x for x in d))
+    expect = []
+    for x in d:
+        y = x / nrm
+        for _ in range(5):
+            y = HP.ns_a * y + HP.ns_b * y * y * y + HP.ns_c * y * y * y * y * y
+        expect.append(y)
+    out = O.newton_schulz(np.diag(d))
+    for i in range(4):
+        for j in range(4):
+            want = expect[i] if i == j else 0.0
+            assert abs(out[i, j] - want) < 1e-12
+
+
+def test_ns5_invariances():
+    rng = np.random.default_rng(3)
+    m = rng.standard_normal((20, 36))
+    o = O.newton_schulz(m)
+    assert rel_fro(O.newton_schulz(4.2 * m), o) < 1e-10            # scale invariance
+    assert rel_fro(O.newton_schulz(-m), -o) < 1e-10                 # odd map
+    assert rel_fro(O.newton_schulz(m.T), o.T) < 1e-10               # transpose equivariance
+    p, _ = np.linalg.qr(rng.standard_normal((20, 20)))
+    q, _ = np.linalg.qr(rng.standard_normal((36, 36)))
+    assert rel_fro(O.newton_schulz(p @ m @ q), p @ o @ q) < 1e-10   # orthogonal equivariance
+
+
+def test_ns5_zero_matrix_gives_zero():
+    assert np.all(O.newton_schulz(np.zeros((5, 9))) == 0.0)
+
+
+def test_lemma1_update_rms():
+    """Exact RMS(O)^2 = sum f^5(sigma_i)^2 / (A B); the band holds when sigma_i/||M|| >= 2e-3."""
+    for shape in [(128, 512), (512, 128), (96, 96)]:
+        m = gaussian(shape, 5)
+        o = O.newton_schulz(m)
+        s = np.linalg.svd(m, compute_uv=False)
+        exact = math.sqrt(float(np.sum(f_poly_composed(s / np.linalg.norm(s)) ** 2)) / (shape[0] * shape[1]))
+        rms = math.sqrt(float(np.mean(o * o)))
+        assert abs(rms - exact) < 1e-10 * exact
+        if np.min(s / np.linalg.norm(s)) >= 2e-3:
+            assert 0.68 <= rms * math.sqrt(max(shape)) <= 1.21
+
+
+# ------------------------------------------------------------------ RowNorm ----
+
+def test_rownorm_unit_norms_and_rms_law():
+    rng = np.random.default_rng(9)
+    for shape in [(8, 32), (32, 8), (16, 16), (1, 5), (5, 1)]:
+        m = rng.standard_normal(shape)
+        r = O.row_normalise(m)
+        axis = 0 if shape[0] > shape[1] else 1
+        assert np.max(np.abs(np.linalg.norm(r, axis=axis) - 1.0)) < 1e-12
+        assert abs(math.sqrt(float(np.mean(r * r))) - math.sqrt(1 / max(shape))) < 1e-12
+        assert np.all(np.sign(r) == np.sign(m))
+        assert rel_fro(O.row_normalise(7.0 * m), r) < 1e-14
+
+
+def test_rownorm_bruteforce_loops_and_zero_lines():
+    m = [[3.0, 4.0, 0.0], [0.0, 0.0, 0.0]]            # flat: rows
+    out = O.row_normalise(np.array(m))
+    assert out.tolist() == [[0.6, 0.8, 0.0], [0.0, 0.0, 0.0]]
+    t = [[1.0, 0.0], [2.0, 0.0], [2.0, 0.0]]           # tall: columns
+    out = O.row_normalise(np.array(t))
+    want = [[1 / 3, 0.0], [2 / 3, 0.0], [2 / 3, 0.0]]
+    for i in range(3):
+        for j in range(2):
+            assert abs(out[i, j] - want[i][j]) < 1e-15
+
+
+def test_gamma_one_rownorm_rms_equals_lemma1_rms():
+    """With gamma = 1 the RowNorm direction has RMS sqrt(1/max(A,B)), Lemma 1's value."""
+    for shape in [(24, 40), (40, 24)]:
+        m = gaussian(shape, 2)
+        hp1 = O.OracleHParams(gamma=1.0)
+        r = O.rownorm_update_direction(m, hp1)
+        assert abs(math.sqrt(float(np.mean(r * r))) * math.sqrt(max(shape)) - 1.0) < 1e-12
+
+
+# ------------------------------------------------------- momentum and update ----
+
+def test_momentum_geometric_series():
+    """Constant gradient from M_0 = 0: M_t = G (1 - mu^t) / (1 - mu)."""
+    g = gaussian((3, 4), 1)
+    m = np.zeros_like(g)
+    for t in range(1, 8):
+        m = O.momentum(m, g, HP.mu)
+        assert np.max(np.abs(m - g * (1 - HP.mu ** t) / (1 - HP.mu))) < 1e-13
+    assert np.array_equal(O.momentum(np.ones((2, 2)), np.zeros((2, 2)), 0.5), np.full((2, 2), 0.5))
+
+
+def test_weight_decay_alone():
+    w = gaussian((6, 10), 4)
+    for step in (0, 1, 2):
+        w1, m1 = O.muon_step(w, np.zeros_like(w), np.zeros_like(w), step, HP)
+        assert np.all(m1 == 0.0)
+        assert np.max(np.abs(w1 - (1 - HP.lr * HP.weight_decay) * w)) < 1e-15
+
+
+@pytest.mark.parametrize("shape", [(128, 512), (512, 128), (64, 64)])
+def test_w0_probe_refresh_step_closed_form(shape):
+    """W = 0 isolates the update: W' = -lr * 0.2 * sqrt(max(A,B)) * O."""
+    mp, g = gaussian(shape, 21), gaussian(shape, 22)
+    w1, m1 = O.muon_step(np.zeros(shape), mp, g, 0, HP)
+    expect = -HP.lr * 0.2 * math.sqrt(max(shape)) * svd_closed_form(HP.mu * mp + g)
+    assert rel_fro(w1, expect) < 1e-10
+
+
+def test_w0_probe_rownorm_step_and_gamma_linearity():
+    shape = (40, 24)
+    mp, g = gaussian(shape, 31), gaussian(shape, 32)
+    w1, m1 = O.muon_step(np.zeros(shape), mp, g, 1, HP)
+    m = HP.mu * mp + g
+    expect = -HP.lr * 0.2 * math.sqrt(40) * HP.gamma * (m / np.linalg.norm(m, axis=0, keepdims=True))
+    assert rel_fro(w1, expect) < 1e-13
+    hp2 = O.OracleHParams(gamma=2 * HP.gamma)
+    w2, _ = O.muon_step(np.zeros(shape), mp, g, 1, hp2)
+    assert rel_fro(w2, 2 * w1) < 1e-14
+
+
+def test_k1_periodic_is_vanilla_bitwise():
+    rng = np.random.default_rng(5)
+    shape = (16, 24)
+    w_a = w_b = rng.standard_normal(shape) * 0.02
+    m_a = m_b = np.zeros(shape)
+    hp1 = O.OracleHParams(period_k=1)
+    for s in range(5):
+        g = rng.standard_normal(shape) * 1e-3
+        w_a, m_a = O.muon_step(w_a, m_a, g, s, hp1)
+        w_b, m_b = O.vanilla_step(w_b, m_b, g, HP)
+        assert np.array_equal(w_a, w_b) and np.array_equal(m_a, m_b)
+
+
+def test_periodic_twelve_steps_dispatch():
+    """K = 3 over 12 steps: refresh steps equal vanilla steps, the rest RowNorm steps."""
+    rng = np.random.default_rng(6)
+    shape = (12, 20)
+    w = rng.standard_normal(shape) * 0.02
+    m = np.zeros(shape)
+    for s in range(12):
+        g = rng.standard_normal(shape) * 1e-3
+        w_p, m_p = O.muon_step(w, m, g, s, HP)
+        ref = O.vanilla_step(w, m, g, HP) if s % 3 == 0 else O.rownorm_step(w, m, g, HP)
+        assert np.array_equal(w_p, ref[0]) and np.array_equal(m_p, ref[1])
+        w, m = w_p, m_p
+
+
+# ---------------------------------------------------- planted-mistake check ----
+
+def _ns_variant(m, mistake):
+    """Copies of the iteration with one planted mistake each (CPU only, flat inputs)."""
+    a, b, c = HP.ns_a, HP.ns_b, HP.ns_c
+    x = np.asarray(m, dtype=np.float64)
+    x = x / np.linalg.norm(x)
+    for _ in range(5 if mistake != "four_steps" else 4):
+        if mistake == "gram_transposed":
+            s = x.T @ x                                  # X^T X where X X^T belongs
+            x = a * x + b * (s @ x) + c * (s @ s @ x)
+            continue
+        s = x @ x.T
+        if mistake == "sign_b":
+            x = a * x - b * (s @ x) + c * (s @ s @ x)
+        elif mistake == "drop_c":
+            x = a * x + b * (s @ x)
+        elif mistake == "c_on_s":
+            x = a * x + b * (s @ x) + c * (s @ x)
+        else:
+            x = a * x + b * (s @ x) + c * (s @ s @ x)
+    return x
+
+
+@pytest.mark.parametrize("mistake", ["sign_b", "drop_c", "c_on_s", "four_steps", "gram_transposed"])
+def test_pins_reject_planted_mistakes(mistake):
+    m = gaussian((16, 16) if mistake == "gram_transposed" else (12, 30), 77)
+    assert rel_fro(_ns_variant(m, "none"), svd_closed_form(m)) < 1e-10
+    assert rel_fro(_ns_variant(m, mistake), svd_closed_form(m)) > 1e-3
+
+
+def test_pins_reject_planted_rownorm_and_update_mistakes():
+    m = gaussian((10, 25), 78)
+    wrong_axis = m / np.linalg.norm(m, axis=0, keepdims=True)
+    r = O.row_normalise(m)
+    assert np.max(np.abs(np.linalg.norm(r, axis=1) - 1)) < 1e-12
+    assert np.max(np.abs(np.linalg.norm(wrong_axis, axis=1) - 1)) > 1e-2
+    # an update scaled by max(A,B) instead of its square root fails the W = 0 probe pin
+    mp, g = gaussian((10, 25), 79), gaussian((10, 25), 80)
+    good = -HP.lr * 0.2 * math.sqrt(25) * svd_closed_form(HP.mu * mp + g)
+    bad = -HP.lr * 0.2 * 25 * svd_closed_form(HP.mu * mp + g)
+    w1, _ = O.muon_step(np.zeros((10, 25)), mp, g, 0, HP)
+    assert rel_fro(w1, good) < 1e-10 and rel_fro(bad, good) > 1.0
