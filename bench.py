@@ -1,0 +1,258 @@
+"""Benchmark of the Periodic Row-wise Muon step on one MI355X.
+
+One bench step is one Periodic cycle of K = 3 optimizer steps over the whole
+layer set: an NS5 refresh step (momentum, Newton-Schulz, Eq. 4 update) followed
+by K - 1 RowNorm steps; together they run every stage of the path. The default
+workload is the 15B-scale layer set at H = 5120 (both streams: qkv [15360,5120],
+proj [5120,5120], MLP [20480,5120] and [5120,20480], modulation [30720,5120];
+944 M fp32 elements per state tensor), gradients 1e-3 * Student-t(3), all state
+resident in HBM.
+
+Prints ONE JSON line. `value` is the mean time of one Muon optimizer step
+averaged over the Periodic cycle (ms, lower is better); `ms_per_step` is the time
+of one whole cycle. Also reported: the vanilla (every step NS5) step time, NS5
+TFLOP/s, RowNorm GB/s, the dominant kernel against its roofline (per-launch
+HIP-event durations recorded by the library on the launch stream), and the
+float64 oracle timed on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Muon step ms per DiT block set; NS5 MFMA TFLOP/s; RowNorm HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def ns5_flops_sym(m, n, steps=5):
+    """Algorithmic NS5 flops counting only the symmetric halves of X X^T and A A."""
+    return steps * (3.0 * m * m * n + 1.0 * m ** 3)
+
+
+def apply_flops(m, n):
+    """The B X product of one iteration: [m, m] x [m, n]."""
+    return 2.0 * m * m * n
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=8, help="timed Periodic cycles")
+    ap.add_argument("--warmup", type=int, default=2, help="untimed Periodic cycles")
+    ap.add_argument("--workload", default="15b", choices=["15b", "mmdit3072", "bucket2048", "dit2048"])
+    ap.add_argument("--vanilla-steps", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def pick_workload(name):
+    from matrix_orthogonalising_optimizer_02_amd import workloads as WL
+    return {"15b": WL.LAYER_SET_15B_H5120, "mmdit3072": WL.MMDIT_PAIR_H3072,
+            "bucket2048": WL.MIXED_BUCKET_H2048, "dit2048": WL.DIT_BLOCK_H2048}[name]
+
+
+def cpu_baseline(wl, k):
+    """Time the float64 oracle on the workload's smallest matrix and scale to the set.
+
+    Sample: one refresh step and one RowNorm step of the oracle on one matrix.
+    The refresh time is scaled by the oracle's own flop count (Eq. 2 as written:
+    X X^T, A X and A (A X), 8 m^2 n per iteration) and the RowNorm time by elements.
+    """
+    import numpy as np
+    from oracle import muon_oracle as O
+    from matrix_orthogonalising_optimizer_02_amd import workloads as WL
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    idx = min(range(len(wl.shapes)), key=lambda i: wl.shapes[i][0] * wl.shapes[i][1])
+    shape = wl.shapes[idx]
+    w, m, g = WL.host_inputs(wl, idx)
+    hp = O.OracleHParams(period_k=k)
+    t0 = time.perf_counter()
+    O.vanilla_step(w, m, g, hp)
+    t_ref = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.rownorm_step(w, m, g, hp)
+    t_rn = time.perf_counter() - t0
+
+    def oflops(s):
+        mm, nn = min(s), max(s)
+        return hp.ns_steps * 8.0 * mm * mm * nn
+
+    ref_total = t_ref * sum(oflops(s) for s in wl.shapes) / oflops(shape)
+    rn_total = t_rn * wl.elements / (shape[0] * shape[1])
+    avg_ms = 1e3 * (ref_total + (k - 1) * rn_total) / k
+    return {"value": round(avg_ms, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle refresh step ({t_ref:.1f} s) and RowNorm step ({t_rn:.2f} s) on the "
+                      f"{shape[0]}x{shape[1]} matrix, scaled by flops and elements to the {len(wl.shapes)}-matrix "
+                      f"set; value = mean ms per optimizer step over a K={k} cycle",
+            "vanilla_step_ms": round(1e3 * ref_total, 1), "rownorm_step_ms": round(1e3 * rn_total, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "
+              "(one GPU's share of the sharded step is what it measures)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import matrix_orthogonalising_optimizer_02_amd as pkg
+    from matrix_orthogonalising_optimizer_02_amd import workloads as WL
+
+    def say(msg):
+        if not args.quiet:
+            print(msg, file=sys.stderr, flush=True)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pkg.load_library()
+    dev = torch.device("cuda:0")
+    wl = pick_workload(args.workload)
+    k = 3
+    shapes = list(wl.shapes)
+    say(f"workload: {wl.name}, {len(shapes)} matrices, {wl.elements / 1e6:.0f} M elements")
+
+    weights = [torch.empty(s, dtype=torch.float32, device=dev) for s in shapes]
+    momenta = [torch.zeros(s, dtype=torch.float32, device=dev) for s in shapes]
+    for i, w in enumerate(weights):
+        WL.device_fill(w, wl.key, WL.ROLE_W, i, wl.w_std)
+    grads = []
+    for step in range(k):
+        gs = [torch.empty(s, dtype=torch.float32, device=dev) for s in shapes]
+        for i, g in enumerate(gs):
+            WL.device_fill(g, wl.key, WL.ROLE_G, i, wl.g_std, wl.g_dist, step)
+        grads.append(gs)
+    ws = pkg.make_workspace(shapes, dev)
+    torch.cuda.synchronize()
+    say(f"inputs resident: workspace {ws.numel() / 2**30:.2f} GiB")
+
+    hp = pkg.default_hparams(period_k=k)
+    hp_vanilla = pkg.default_hparams(period_k=1)
+    step_counter = [0]
+
+    def cycle():
+        for j in range(k):
+            pkg.muon_step(weights, momenta, grads[j], step_counter[0], hp, ws)
+            step_counter[0] += 1
+
+    for _ in range(args.warmup):
+        cycle()
+    torch.cuda.synchronize()
+    say(f"warmup done ({args.warmup} cycles)")
+
+    # ---- timed region: Periodic cycles, per-kernel events recorded by the library
+    pkg.timing_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        cycle()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = pkg.timing_read()
+    pkg.timing_enable(False)
+    cycle_ms = ev0.elapsed_time(ev1) / args.steps
+    say(f"periodic: {cycle_ms:.3f} ms per cycle (wall {1e3 * wall / args.steps:.3f} ms)")
+
+    # ---- vanilla steps (NS5 every step) for the Periodic saving
+    torch.cuda.synchronize()
+    ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev2.record()
+    for j in range(args.vanilla_steps):
+        pkg.muon_step(weights, momenta, grads[j % k], 0, hp_vanilla, ws)
+    ev3.record()
+    torch.cuda.synchronize()
+    vanilla_ms = ev2.elapsed_time(ev3) / max(args.vanilla_steps, 1)
+    say(f"vanilla: {vanilla_ms:.3f} ms per step")
+
+    refreshes = args.steps
+    rownorm_steps = args.steps * (k - 1)
+    ms = {name: kern[name][0] for name in kern}
+    cnt = {name: kern[name][1] for name in kern}
+    ns5_ms = (ms["gram"] + ms["poly"] + ms["apply"] + ms["apply_final"]) / refreshes
+    ns5_flops = sum(ns5_flops_sym(min(s), max(s), hp.ns_steps) for s in shapes)
+    ns5_tflops = ns5_flops / (ns5_ms * 1e-3) / 1e12
+    rn_ms = (ms["rownorm_rows"] + ms["colnorm_partial"] + ms["colnorm_finalize"] + ms["colnorm_apply"]) / rownorm_steps
+    rn_gbs = 20.0 * wl.elements / (rn_ms * 1e-3) / 1e9
+    # dominant kernel: the B X product of iterations 1..N-1
+    apply_launch_ms = ms["apply"] / max(cnt["apply"], 1)
+    apply_launch_flops = sum(apply_flops(min(s), max(s)) for s in shapes)
+    apply_tflops = apply_launch_flops / (apply_launch_ms * 1e-3) / 1e12
+    kernels = {}
+    for name in kern:
+        if cnt[name]:
+            kernels[name] = {"launches": cnt[name], "avg_ms": round(ms[name] / cnt[name], 4),
+                             "total_ms_per_cycle": round(ms[name] / args.steps, 4)}
+    for name, fl in (("gram", lambda m, n: m * m * n), ("poly", lambda m, n: 1.0 * m ** 3),
+                     ("apply", apply_flops), ("apply_final", apply_flops)):
+        if cnt[name]:
+            f = sum(fl(min(s), max(s)) for s in shapes)
+            kernels[name]["algorithmic_tflops"] = round(f / (ms[name] / cnt[name] * 1e-3) / 1e12, 1)
+    elems_flat = sum(a * b for a, b in shapes if a <= b)
+    elems_tall = wl.elements - elems_flat
+    if cnt["rownorm_rows"]:
+        kernels["rownorm_rows"]["algorithmic_gbs"] = round(
+            20.0 * elems_flat / (ms["rownorm_rows"] / cnt["rownorm_rows"] * 1e-3) / 1e9, 1)
+    if cnt["colnorm_partial"]:
+        kernels["colnorm_partial"]["algorithmic_gbs"] = round(
+            12.0 * elems_tall / (ms["colnorm_partial"] / cnt["colnorm_partial"] * 1e-3) / 1e9, 1)
+        kernels["colnorm_apply"]["algorithmic_gbs"] = round(
+            12.0 * elems_tall / (ms["colnorm_apply"] / cnt["colnorm_apply"] * 1e-3) / 1e9, 1)
+    if cnt["cast"]:
+        kernels["cast"]["algorithmic_gbs"] = round(
+            16.0 * wl.elements / (ms["cast"] / cnt["cast"] * 1e-3) / 1e9, 1)
+
+    out = {
+        "metric": METRIC,
+        "value": round(cycle_ms / k, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(cycle_ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+fp32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "matrices": len(shapes), "elements": wl.elements,
+                   "shapes": [list(s) for s in shapes], "period_k": k, "gamma": hp.gamma,
+                   "ns_steps": hp.ns_steps, "step": "one Periodic cycle = 1 NS5 refresh + 2 RowNorm steps"},
+        "muon_step_ms_periodic_avg": round(cycle_ms / k, 4),
+        "muon_step_ms_vanilla": round(vanilla_ms, 4),
+        "periodic_saving_pct": round(100.0 * (1.0 - (cycle_ms / k) / vanilla_ms), 1),
+        "ns5_ms_per_refresh": round(ns5_ms, 4),
+        "ns5_tflops": round(ns5_tflops, 1),
+        "ns5_frac_of_bf16_peak": round(ns5_tflops / PEAK_BF16_TFLOPS, 4),
+        "rownorm_step_ms": round(rn_ms, 4),
+        "rownorm_gbs": round(rn_gbs, 1),
+        "rownorm_frac_of_hbm_peak": round(rn_gbs / PEAK_HBM_GBS, 4),
+        "roofline": {"bound": "mfma", "kernel": "k_ns_gemm<apply> (B X, iterations 1..4)",
+                     "achieved": round(apply_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(apply_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "launch_ms": round(apply_launch_ms, 4), "launch_flops": apply_launch_flops},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        say("cpu baseline: timing the float64 oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline(wl, k)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,152 @@
+/*
+ * muon_rocm.h -- C ABI of the MI355X (gfx950) Muon optimizer-step library.
+ *
+ * The library applies, to a set of 2-D fp32 weight matrices W of shape [A, B],
+ *   - the Muon step of "Muon is Scalable for LLM Training" (Sec. 2.1 Eq. 1 momentum,
+ *     Eq. 2 Newton-Schulz with X0 = M / ||M||_F and coefficients a, b, c, and
+ *     Sec. 2.2 Eq. 4 update W <- W - lr * (0.2 * O * sqrt(max(A,B)) + wd * W)), and
+ *   - the Periodic Row-wise variant of "Scaling Muon for Diffusion Transformers"
+ *     (Periodic Row-wise paragraphs): NS5 once every K steps, and on the other steps
+ *     Eq. 4 with O replaced by gamma * RowNorm(M), RowNorm scaling every row of M
+ *     to unit l2 norm when A <= B and every column when A > B.
+ * Tall matrices (A > B) run Newton-Schulz on M^T so the Gram matrix is min(A,B)^2.
+ *
+ * Conventions shared by every entry point:
+ *   - All matrix buffers are DEVICE pointers owned by the caller, fp32, row-major,
+ *     contiguous (leading dimension = cols), 16-byte aligned.
+ *   - `workspace` is a caller-owned DEVICE buffer of at least the size that
+ *     muon_workspace_bytes() reports for the same shapes, 256-byte aligned. Its
+ *     contents need not be initialised and are garbage after the call.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream). Calls only
+ *     enqueue work on it and never synchronise; results are ready when the stream
+ *     reaches that point. Concurrent calls must use distinct workspaces.
+ *   - Every argument is validated on the host before anything is enqueued: on any
+ *     error code no kernel runs and no buffer is touched.
+ *   - Matrices with rows == 0 or cols == 0 are skipped (their pointers may be NULL);
+ *     count == 0 is a no-op.
+ *   - NaN / Inf in the inputs propagate to the outputs; they are not checked.
+ *   - Results are deterministic: identical inputs give bitwise identical outputs.
+ */
+#ifndef MUON_ROCM_H
+#define MUON_ROCM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MUON_ABI_VERSION 1
+
+/* Status codes returned by every entry point. */
+#define MUON_OK 0
+#define MUON_ERR_INVALID_ARG (-1) /* NULL where a pointer is required, negative dims,
+                                     count < 0, ns_steps < 1, period_k < 1, eps <= 0 */
+#define MUON_ERR_WORKSPACE (-2)   /* workspace NULL or smaller than required */
+#define MUON_ERR_ALIGN (-3)       /* matrix pointer not 16-byte aligned, workspace not 256 */
+#define MUON_ERR_ALIAS (-4)       /* overlapping buffers that must be distinct */
+#define MUON_ERR_HIP (-5)         /* a HIP runtime call or kernel launch failed */
+#define MUON_ERR_TOO_LARGE (-6)   /* a dimension above 2^30 or a matrix above 2^40 elements */
+
+/* Hyperparameters. muon_default_hparams() fills the pages' defaults:
+ * lr 1e-3, weight_decay 0.1, mu 0.95 (Muon notes Sec. 2.2), a, b, c =
+ * 3.4445, -4.7750, 2.0315 (Sec. 2.1), rms_scale 0.2 (Eq. 4), gamma 0.15 and
+ * period_k 3 (DiT paper, K/gamma sweep), eps 1e-7, ns_steps 5 (Sec. 2.2). */
+typedef struct muon_hparams {
+    float lr;           /* eta */
+    float weight_decay; /* lambda, decoupled (Eq. 3/4) */
+    float mu;           /* momentum coefficient (Eq. 1) */
+    float ns_a, ns_b, ns_c; /* Newton-Schulz polynomial coefficients (Eq. 2) */
+    float rms_scale;    /* the 0.2 of Eq. 4 */
+    float gamma;        /* RowNorm step relative to NS5 (Periodic variant) */
+    float eps;          /* norms are divided as x / max(norm, eps) */
+    int32_t ns_steps;   /* N, Newton-Schulz iterations (>= 1) */
+    int32_t period_k;   /* K, refresh period (>= 1; 1 = vanilla Muon) */
+} muon_hparams;
+
+/* One weight matrix with its optimizer state. All three are [rows, cols]. */
+typedef struct muon_matrix {
+    int64_t rows, cols;
+    float* w;       /* weights, updated in place */
+    float* m;       /* momentum (M_{t-1} in, M_t out), updated in place; zeros at t = 0 */
+    const float* g; /* gradient, read only */
+} muon_matrix;
+
+/* Kernel classes reported by the optional timing facility. */
+#define MUON_KCLASS_CAST 0          /* momentum + Frobenius partials + bf16 working copies */
+#define MUON_KCLASS_FROB 1          /* per-matrix 1 / max(||M||_F, eps) */
+#define MUON_KCLASS_GRAM 2          /* A = X X^T (symmetric tiles, bf16 MFMA) */
+#define MUON_KCLASS_POLY 3          /* B = b A + c A A (symmetric tiles, bf16 MFMA) */
+#define MUON_KCLASS_APPLY 4         /* X' = a X + B X, iterations 1..N-1 */
+#define MUON_KCLASS_APPLY_FINAL 5   /* last iteration: O out, or the fused Eq. 4 update */
+#define MUON_KCLASS_ROWNORM_ROWS 6  /* one-pass RowNorm step, flat / square matrices */
+#define MUON_KCLASS_COLNORM_PARTIAL 7  /* tall: momentum + per-column partial sums */
+#define MUON_KCLASS_COLNORM_FINALIZE 8 /* tall: per-column 1 / max(norm, eps) */
+#define MUON_KCLASS_COLNORM_APPLY 9    /* tall: Eq. 4 update with the column-normalised M */
+#define MUON_KCLASS_COUNT 10
+
+/* Returns MUON_ABI_VERSION. Host only. */
+int muon_abi_version(void);
+
+/* Static English text for a status code (never NULL). Host only. */
+const char* muon_status_str(int status);
+
+/* Detail of the last MUON_ERR_HIP (or other error) raised on this thread; "" if none. */
+const char* muon_last_error(void);
+
+/* Fills *hp with the defaults listed above. Host only; hp NULL is ignored. */
+void muon_default_hparams(muon_hparams* hp);
+
+/* Workspace size in bytes sufficient for muon_step, ns5_batched and rownorm_update
+ * on `count` matrices of shapes rows[i] x cols[i]. Host only, touches no device.
+ * Errors: INVALID_ARG (NULL bytes, count < 0, NULL rows/cols with count > 0, negative
+ * dims), TOO_LARGE. */
+int muon_workspace_bytes(const int64_t* rows, const int64_t* cols, int32_t count, size_t* bytes);
+
+/* One optimizer step at 0-based step index `step` for `count` matrices.
+ * Periodic schedule (DiT paper, "NS5 once every K steps"; read here as a refresh
+ * iff step % period_k == 0, so step 0 refreshes and period_k == 1 is vanilla Muon):
+ *   refresh:  M <- mu M + G;  O = NS5(M);  W <- W - lr (rms_scale sqrt(max(A,B)) O + wd W)
+ *   otherwise: exactly rownorm_update() below.
+ * mats: host array of `count` descriptors. Errors: INVALID_ARG, ALIGN, ALIAS (any two
+ * of all w, m, g ranges overlap), WORKSPACE, TOO_LARGE, HIP. */
+int muon_step(const muon_matrix* mats, int32_t count, const muon_hparams* hp, int64_t step,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Newton-Schulz orthogonalisation alone ("Muon is Scalable", Sec. 2.1 Eq. 2):
+ * o_out[i] = NS_N(m_in[i]) with X0 = M / max(||M||_F, eps), for [rows[i], cols[i]]
+ * fp32 device matrices; the output has the input's shape and orientation. bf16 MFMA
+ * products with fp32 accumulation; relative Frobenius error vs exact arithmetic is
+ * about 1e-2. o_out[i] == m_in[i] (in place) is allowed; any other overlap is ALIAS.
+ * m_in, o_out, rows, cols are host arrays of `count` entries. Only hp->ns_* and
+ * hp->eps are used. Errors: INVALID_ARG, ALIGN, ALIAS, WORKSPACE, TOO_LARGE, HIP. */
+int ns5_batched(const float* const* m_in, float* const* o_out, const int64_t* rows,
+                const int64_t* cols, int32_t count, const muon_hparams* hp,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* The Periodic variant's non-refresh step (DiT paper, Periodic Row-wise and
+ * distributed-implementation paragraphs), fp32 throughout, in one pass for flat and
+ * square matrices and three short kernels for tall ones:
+ *   M <- mu M + G
+ *   R = M / max(row l2 norms, eps)     if rows <= cols
+ *   R = M / max(column l2 norms, eps)  if rows >  cols
+ *   W <- W - lr (rms_scale gamma sqrt(max(A,B)) R + wd W)
+ * Errors as muon_step. */
+int rownorm_update(const muon_matrix* mats, int32_t count, const muon_hparams* hp,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Optional per-kernel-class timing. While enabled (enable != 0), every kernel the
+ * library enqueues is bracketed by HIP events recorded on the caller's stream.
+ * muon_timing_read() waits for the recorded events, adds their durations into
+ * ms[MUON_KCLASS_COUNT] and launch counts into launches[MUON_KCLASS_COUNT] (either
+ * may be NULL), and clears the record. muon_timing_enable(0) discards the record.
+ * Process-global; not meant for concurrent callers. Errors: HIP. */
+int muon_timing_enable(int enable);
+int muon_timing_read(double* ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_ROCM_H */

@@ -1,0 +1,20 @@
+"""Muon and Periodic Row-wise Muon optimizer steps for 2-D weights on MI355X (gfx950).
+
+The work runs in libmuon_rocm.so (HIP kernels behind a C ABI, include/muon_rocm.h);
+`binding` marshals torch tensors to it. `workloads` holds the seeded synthetic
+inputs used by the tests and the benchmark.
+"""
+from .binding import (  # noqa: F401
+    MuonError,
+    MuonHParams,
+    MuonOptimizer,
+    default_hparams,
+    load_library,
+    make_workspace,
+    muon_step,
+    ns5_batched,
+    rownorm_update,
+    timing_enable,
+    timing_read,
+    workspace_bytes,
+)

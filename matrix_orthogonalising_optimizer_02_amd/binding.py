@@ -1,0 +1,261 @@
+"""ctypes binding of libmuon_rocm.so (include/muon_rocm.h).
+
+Argument marshalling only: every step of the optimizer runs in the library's HIP
+kernels. torch tensors provide device memory and the current HIP stream. If the
+library is not built, or no GPU is present, calls raise; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+from .build import LIB_PATH
+
+MUON_OK = 0
+MUON_ERR_INVALID_ARG = -1
+MUON_ERR_WORKSPACE = -2
+MUON_ERR_ALIGN = -3
+MUON_ERR_ALIAS = -4
+MUON_ERR_HIP = -5
+MUON_ERR_TOO_LARGE = -6
+
+KCLASS_NAMES = ("cast", "frob", "gram", "poly", "apply", "apply_final", "rownorm_rows",
+                "colnorm_partial", "colnorm_finalize", "colnorm_apply")
+
+EXPORTED = ("muon_abi_version", "muon_status_str", "muon_last_error", "muon_default_hparams",
+            "muon_workspace_bytes", "muon_step", "ns5_batched", "rownorm_update",
+            "muon_timing_enable", "muon_timing_read")
+
+
+class MuonHParams(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_float), ("weight_decay", ctypes.c_float), ("mu", ctypes.c_float),
+        ("ns_a", ctypes.c_float), ("ns_b", ctypes.c_float), ("ns_c", ctypes.c_float),
+        ("rms_scale", ctypes.c_float), ("gamma", ctypes.c_float), ("eps", ctypes.c_float),
+        ("ns_steps", ctypes.c_int32), ("period_k", ctypes.c_int32),
+    ]
+
+
+class MuonMatrix(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("w", ctypes.c_void_p),
+                ("m", ctypes.c_void_p), ("g", ctypes.c_void_p)]
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        msg = f"{where}: status {status} ({status_str(status)})"
+        if detail:
+            msg += f": {detail}"
+        super().__init__(msg)
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libmuon_rocm.so (built in-tree by build.build()); raises if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built; run matrix_orthogonalising_optimizer_02_amd.build.build()")
+    lib = ctypes.CDLL(p)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.muon_abi_version.restype = ctypes.c_int
+    lib.muon_status_str.restype = ctypes.c_char_p
+    lib.muon_status_str.argtypes = [ctypes.c_int]
+    lib.muon_last_error.restype = ctypes.c_char_p
+    lib.muon_default_hparams.argtypes = [ctypes.POINTER(MuonHParams)]
+    lib.muon_default_hparams.restype = None
+    lib.muon_workspace_bytes.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64), i32,
+                                         ctypes.POINTER(ctypes.c_size_t)]
+    lib.muon_step.argtypes = [ctypes.POINTER(MuonMatrix), i32, ctypes.POINTER(MuonHParams), i64, vp, sz, vp]
+    lib.ns5_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_int64),
+                                ctypes.POINTER(ctypes.c_int64), i32, ctypes.POINTER(MuonHParams), vp, sz, vp]
+    lib.rownorm_update.argtypes = [ctypes.POINTER(MuonMatrix), i32, ctypes.POINTER(MuonHParams), vp, sz, vp]
+    lib.muon_timing_enable.argtypes = [ctypes.c_int]
+    lib.muon_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    for name in ("muon_step", "ns5_batched", "rownorm_update", "muon_workspace_bytes",
+                 "muon_timing_enable", "muon_timing_read"):
+        getattr(lib, name).restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().muon_status_str(status).decode()
+
+
+def _check(rc: int, where: str):
+    if rc != MUON_OK:
+        detail = load_library().muon_last_error().decode()
+        raise MuonError(rc, where, detail)
+
+
+def default_hparams(**overrides) -> MuonHParams:
+    hp = MuonHParams()
+    load_library().muon_default_hparams(ctypes.byref(hp))
+    for k, v in overrides.items():
+        if not hasattr(hp, k):
+            raise KeyError(k)
+        setattr(hp, k, v)
+    return hp
+
+
+def workspace_bytes(shapes: Sequence[Sequence[int]]) -> int:
+    n = len(shapes)
+    rows = (ctypes.c_int64 * max(n, 1))(*[int(s[0]) for s in shapes])
+    cols = (ctypes.c_int64 * max(n, 1))(*[int(s[1]) for s in shapes])
+    out = ctypes.c_size_t(0)
+    _check(load_library().muon_workspace_bytes(rows, cols, n, ctypes.byref(out)), "muon_workspace_bytes")
+    return int(out.value)
+
+
+# ------------------------------------------------------------ tensor helpers ----
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check_tensor(t, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32 or t.dim() != 2 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 2-D float32 tensor")
+    if t.numel() and t.device.type != "cuda":
+        raise ValueError(f"{name} must live on a GPU")
+
+
+def _stream_handle(stream, device=None):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(int(getattr(stream, "cuda_stream", stream)))
+
+
+def make_workspace(shapes, device="cuda"):
+    """A uint8 device buffer large enough for every entry point on `shapes`."""
+    torch = _torch()
+    return torch.empty(max(workspace_bytes(shapes), 1), dtype=torch.uint8, device=device)
+
+
+def _ws(workspace, shapes, device):
+    if workspace is None:
+        workspace = make_workspace(shapes, device)
+    return ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel())
+
+
+def _matrices(weights, momenta, grads):
+    if not (len(weights) == len(momenta) == len(grads)):
+        raise ValueError("weights, momenta and grads must have the same length")
+    arr = (MuonMatrix * max(len(weights), 1))()
+    for i, (w, m, g) in enumerate(zip(weights, momenta, grads)):
+        for t, nm in ((w, "weight"), (m, "momentum"), (g, "grad")):
+            _check_tensor(t, f"{nm}[{i}]")
+        if not (w.shape == m.shape == g.shape):
+            raise ValueError(f"shape mismatch at index {i}")
+        arr[i] = MuonMatrix(w.shape[0], w.shape[1], w.data_ptr() or None, m.data_ptr() or None,
+                            g.data_ptr() or None)
+    return arr
+
+
+def muon_step(weights, momenta, grads, step: int, hp: Optional[MuonHParams] = None,
+              workspace=None, stream=None):
+    """One Periodic Row-wise Muon step (refresh iff step % period_k == 0), in place."""
+    hp = hp or default_hparams()
+    arr = _matrices(weights, momenta, grads)
+    dev = weights[0].device if weights else None
+    ws, wsb = _ws(workspace, [tuple(w.shape) for w in weights], dev)
+    rc = load_library().muon_step(arr, len(weights), ctypes.byref(hp), int(step), ws, wsb,
+                                  _stream_handle(stream, dev))
+    _check(rc, "muon_step")
+
+
+def rownorm_update(weights, momenta, grads, hp: Optional[MuonHParams] = None, workspace=None,
+                   stream=None):
+    """The Periodic variant's RowNorm step, in place."""
+    hp = hp or default_hparams()
+    arr = _matrices(weights, momenta, grads)
+    dev = weights[0].device if weights else None
+    ws, wsb = _ws(workspace, [tuple(w.shape) for w in weights], dev)
+    rc = load_library().rownorm_update(arr, len(weights), ctypes.byref(hp), ws, wsb,
+                                       _stream_handle(stream, dev))
+    _check(rc, "rownorm_update")
+
+
+def ns5_batched(inputs, outputs=None, hp: Optional[MuonHParams] = None, workspace=None, stream=None):
+    """outputs[i] = NS5(inputs[i]); returns the outputs (new tensors when not given)."""
+    torch = _torch()
+    hp = hp or default_hparams()
+    if outputs is None:
+        outputs = [torch.empty_like(x) for x in inputs]
+    if len(outputs) != len(inputs):
+        raise ValueError("inputs and outputs must have the same length")
+    n = len(inputs)
+    ins = (ctypes.c_void_p * max(n, 1))()
+    outs = (ctypes.c_void_p * max(n, 1))()
+    rows = (ctypes.c_int64 * max(n, 1))()
+    cols = (ctypes.c_int64 * max(n, 1))()
+    for i, (x, o) in enumerate(zip(inputs, outputs)):
+        _check_tensor(x, f"inputs[{i}]")
+        _check_tensor(o, f"outputs[{i}]")
+        if x.shape != o.shape:
+            raise ValueError(f"shape mismatch at index {i}")
+        ins[i] = x.data_ptr() or None
+        outs[i] = o.data_ptr() or None
+        rows[i], cols[i] = x.shape
+    dev = inputs[0].device if inputs else None
+    ws, wsb = _ws(workspace, [tuple(x.shape) for x in inputs], dev)
+    rc = load_library().ns5_batched(ins, outs, rows, cols, n, ctypes.byref(hp), ws, wsb,
+                                    _stream_handle(stream, dev))
+    _check(rc, "ns5_batched")
+    return outputs
+
+
+def timing_enable(enable: bool = True):
+    _check(load_library().muon_timing_enable(1 if enable else 0), "muon_timing_enable")
+
+
+def timing_read():
+    """{kernel class: (total ms, launches)} since the last read; waits for the events."""
+    ms = (ctypes.c_double * len(KCLASS_NAMES))()
+    cnt = (ctypes.c_int64 * len(KCLASS_NAMES))()
+    _check(load_library().muon_timing_read(ms, cnt), "muon_timing_read")
+    return {name: (ms[i], int(cnt[i])) for i, name in enumerate(KCLASS_NAMES)}
+
+
+class MuonOptimizer:
+    """Periodic Row-wise Muon over a list of 2-D fp32 CUDA parameters.
+
+    Holds one momentum buffer per parameter (zeros at step 0), the workspace and the
+    step counter; step(grads) advances every parameter by one optimizer step.
+    """
+
+    def __init__(self, params, hp: Optional[MuonHParams] = None):
+        torch = _torch()
+        self.params = list(params)
+        self.hp = hp or default_hparams()
+        self.momenta = [torch.zeros_like(p) for p in self.params]
+        self.workspace = make_workspace([tuple(p.shape) for p in self.params],
+                                        self.params[0].device if self.params else "cuda")
+        self.step_count = 0
+
+    def step(self, grads, stream=None):
+        muon_step(self.params, self.momenta, list(grads), self.step_count, self.hp,
+                  self.workspace, stream)
+        self.step_count += 1
+
+    def state_dict(self):
+        return {"step": self.step_count, "momenta": [m.clone() for m in self.momenta]}
+
+    def load_state_dict(self, state):
+        self.step_count = int(state["step"])
+        for dst, src in zip(self.momenta, state["momenta"]):
+            dst.copy_(src)
+

@@ -1,0 +1,71 @@
+"""Build libmuon_rocm.so (HIP, gfx950) in-tree with hipcc.
+
+Every source under csrc/ is compiled for gfx950 and linked into one shared
+library next to this file; the Python binding loads it from there.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG_DIR, "csrc")
+LIB_NAME = "libmuon_rocm.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+ARCH = "gfx950"
+
+SOURCES = ["k_elementwise.hip", "k_gemm.hip", "muon_abi.cpp"]
+
+COMMON_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+    f"--offload-arch={ARCH}",
+    # packed fp32 VALU ops stay off: scalar fp32 code is what the kernels are written for
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP toolchain is required to build libmuon_rocm.so")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile all sources and link the shared library; returns its path."""
+    cc = hipcc()
+    tmp = tempfile.mkdtemp(prefix="muon_build_")
+    try:
+        objs = []
+        for src in SOURCES:
+            path = os.path.join(CSRC, src)
+            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+            lang = ["-x", "hip"] if src.endswith(".hip") else []
+            cmd = [cc, *COMMON_FLAGS, *lang, "-c", path, "-o", obj]
+            _run(cmd, verbose)
+            objs.append(obj)
+        out_tmp = LIB_PATH + ".tmp"
+        _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", out_tmp], verbose)
+        os.replace(out_tmp, LIB_PATH)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return LIB_PATH
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature; harmless
+    lines = [ln for ln in res.stdout.splitlines() if "packed-fp32-ops" not in ln]
+    if res.returncode != 0:
+        raise RuntimeError("build failed:\n" + " ".join(cmd) + "\n" + "\n".join(lines))
+    if verbose and lines:
+        print("\n".join(lines), flush=True)
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

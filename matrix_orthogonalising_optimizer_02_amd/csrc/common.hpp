@@ -1,0 +1,68 @@
+// Shared device helpers and launch descriptors for the gfx950 Muon kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+// Maximum matrices per grouped launch: descriptors travel in the kernel-argument
+// segment, so a launch needs no host-to-device copy.
+constexpr int kMaxGroup = 16;
+// Working dimensions are padded to this multiple (zeros), so every NS5 GEMM tile
+// and K step is full and the GEMMs need no bounds checks.
+constexpr int kPad = 256;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ unsigned short f2bf(float x) {
+    __bf16 b = (__bf16)x;  // IEEE round-to-nearest-even
+    return __builtin_bit_cast(unsigned short, b);
+}
+
+__device__ __forceinline__ float bf2f(unsigned short u) {
+    return __uint_as_float(((unsigned)u) << 16);
+}
+
+__device__ __forceinline__ unsigned pack2(unsigned short lo, unsigned short hi) {
+    return (unsigned)lo | ((unsigned)hi << 16);
+}
+
+// max(x, eps) that keeps a NaN x (fmaxf would return eps), so NaN norms propagate.
+__device__ __forceinline__ float max_keep_nan(float x, float eps) { return x < eps ? eps : x; }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Fixed-order sum over a 256-thread block; every thread gets the result.
+__device__ __forceinline__ float block_sum_256(float v, float* red /* >= 4 floats of LDS */) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float s = ((red[0] + red[1]) + (red[2] + red[3]));
+    __syncthreads();
+    return s;
+}
+
+// Map a block index to a logical work index so that each XCD (blocks are dealt
+// round-robin over the 8 XCDs) receives one contiguous range of logical indices;
+// neighbouring tiles then share operands in the same L2.
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+    const int q = total >> 3, r = total & 7, x = b & 7, loc = b >> 3;
+    return x * q + (x < r ? x : r) + loc;
+}
+
+}  // namespace muon

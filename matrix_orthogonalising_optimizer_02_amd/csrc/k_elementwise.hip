@@ -1,0 +1,375 @@
+// HBM-bound kernels of the Muon step: momentum + Frobenius partials + bf16 working
+// copies, the Frobenius finalise, and the RowNorm step (rows for flat and square
+// matrices in one pass, columns for tall matrices in three short kernels).
+//
+// Method sources: "Muon is Scalable for LLM Training" Sec. 2.1 Eq. 1 (momentum) and
+// the Newton-Schulz paragraph (X0 = M / ||M||_F); "Scaling Muon for Diffusion
+// Transformers", Periodic Row-wise and distributed-implementation paragraphs
+// (RowNorm of the current momentum: rows of flat matrices, per-column norms of tall
+// ones). Every reduction runs in a fixed order, so results are bitwise repeatable.
+#include "launch.hpp"
+
+namespace muon {
+
+template <typename Desc>
+__device__ __forceinline__ int find_group(const Desc* d, int n, int t) {
+    int g = 0;
+    while (g + 1 < n && t >= d[g + 1].tile_begin) ++g;
+    return g;
+}
+
+// ------------------------------------------------------------------ cast ----
+__global__ __launch_bounds__(256) void k_cast(CastArgs args) {
+    __shared__ unsigned short tile[64][64 + 2];
+    __shared__ float red[4];
+    const int t = blockIdx.x;
+    const int gi = find_group(args.d, args.n, t);
+    const CastDesc& d = args.d[gi];
+    const int local = t - d.tile_begin;
+    const int tr = local / d.tiles_c, tc = local - tr * d.tiles_c;
+    const int tid = threadIdx.x;
+    const int c4 = tid & 15, rq = tid >> 4;
+    const int c0 = tc * 64 + c4 * 4;
+    const bool vec = (d.cols & 3) == 0;
+    const bool mom = args.use_momentum != 0;
+    const float mu = args.mu;
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int rl = rq + 16 * q;
+        const int r = tr * 64 + rl;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (r < d.rows) {
+            const int64_t base = (int64_t)r * d.cols;
+            if (vec && c0 + 3 < d.cols) {
+                float4 mm = *reinterpret_cast<const float4*>(d.m_in + base + c0);
+                if (mom) {
+                    const float4 gg = *reinterpret_cast<const float4*>(d.g + base + c0);
+                    mm.x = fmaf(mu, mm.x, gg.x);
+                    mm.y = fmaf(mu, mm.y, gg.y);
+                    mm.z = fmaf(mu, mm.z, gg.z);
+                    mm.w = fmaf(mu, mm.w, gg.w);
+                }
+                if (d.m_out) *reinterpret_cast<float4*>(d.m_out + base + c0) = mm;
+                v[0] = mm.x; v[1] = mm.y; v[2] = mm.z; v[3] = mm.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = c0 + e;
+                    if (c < d.cols) {
+                        float x = d.m_in[base + c];
+                        if (mom) x = fmaf(mu, x, d.g[base + c]);
+                        if (d.m_out) d.m_out[base + c] = x;
+                        v[e] = x;
+                    }
+                }
+            }
+        }
+        ss = fmaf(v[0], v[0], ss);
+        ss = fmaf(v[1], v[1], ss);
+        ss = fmaf(v[2], v[2], ss);
+        ss = fmaf(v[3], v[3], ss);
+        unsigned short h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[e] = f2bf(v[e]);
+            tile[rl][c4 * 4 + e] = h[e];
+        }
+        uint2 packed;
+        packed.x = pack2(h[0], h[1]);
+        packed.y = pack2(h[2], h[3]);
+        *reinterpret_cast<uint2*>(d.direct + (int64_t)r * d.cols_p + c0) = packed;
+    }
+    __syncthreads();
+    {
+        // transposed copy: output row = input column oc, 16 consecutive input rows
+        const int oc = tid >> 2, ob = (tid & 3) * 16;
+        unsigned w8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w8[e] = pack2(tile[ob + 2 * e][oc], tile[ob + 2 * e + 1][oc]);
+        unsigned short* dst = d.transp + (int64_t)(tc * 64 + oc) * d.rows_p + tr * 64 + ob;
+        reinterpret_cast<uint4*>(dst)[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
+        reinterpret_cast<uint4*>(dst)[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
+    }
+    const float s = block_sum_256(ss, red);
+    if (tid == 0) d.partial[local] = s;
+}
+
+hipError_t launch_cast(const CastArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(k_cast, dim3(a.total), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ frob ----
+__global__ __launch_bounds__(256) void k_frob(FrobArgs args) {
+    __shared__ double red[4];
+    const int g = blockIdx.x;
+    const float* p = args.partial[g];
+    const int n = args.count[g];
+    double acc = 0.0;
+    for (int i = threadIdx.x; i < n; i += 256) acc += (double)p[i];
+    acc = wave_sum_d(acc);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const double tot = (red[0] + red[1]) + (red[2] + red[3]);
+        const float nrm = (float)sqrt(tot);
+        *args.scale[g] = 1.0f / max_keep_nan(nrm, args.eps);
+    }
+}
+
+hipError_t launch_frob(const FrobArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(k_frob, dim3(a.n), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// --------------------------------------------------------- rownorm (rows) ----
+// One 256-thread block per row; the row's M' stays in registers between the norm
+// reduction and the weight update, so every element moves exactly once:
+// read M, G, W and write M, W (20 bytes per element).
+template <int VMAX, bool VEC>
+__global__ __launch_bounds__(256) void k_rownorm_rows(RowArgs args) {
+    __shared__ float red[4];
+    const int t = blockIdx.x;
+    int gi = 0;
+    while (gi + 1 < args.n && t >= args.d[gi + 1].row_begin) ++gi;
+    const RowDesc& d = args.d[gi];
+    const int row = t - d.row_begin;
+    const int tid = threadIdx.x;
+    const int64_t base = (int64_t)row * d.cols;
+    const float mu = args.mu;
+    float ss = 0.f;
+    if constexpr (VEC) {
+        float4 mv[VMAX];
+        const float4* gp = reinterpret_cast<const float4*>(d.g + base);
+        float4* mp = reinterpret_cast<float4*>(d.m + base);
+        float4* wp = reinterpret_cast<float4*>(d.w + base);
+        const int nv = d.cols >> 2;
+#pragma unroll
+        for (int k = 0; k < VMAX; ++k) {
+            const int idx = k * 256 + tid;
+            if (idx < nv) {
+                float4 m = mp[idx];
+                const float4 g = gp[idx];
+                m.x = fmaf(mu, m.x, g.x);
+                m.y = fmaf(mu, m.y, g.y);
+                m.z = fmaf(mu, m.z, g.z);
+                m.w = fmaf(mu, m.w, g.w);
+                mp[idx] = m;
+                mv[k] = m;
+                ss = fmaf(m.x, m.x, ss);
+                ss = fmaf(m.y, m.y, ss);
+                ss = fmaf(m.z, m.z, ss);
+                ss = fmaf(m.w, m.w, ss);
+            }
+        }
+        const float tot = block_sum_256(ss, red);
+        const float c = d.coef / max_keep_nan(sqrtf(tot), args.eps);
+        const float decay = args.decay;
+#pragma unroll
+        for (int k = 0; k < VMAX; ++k) {
+            const int idx = k * 256 + tid;
+            if (idx < nv) {
+                float4 w = wp[idx];
+                w.x = fmaf(-c, mv[k].x, w.x * decay);
+                w.y = fmaf(-c, mv[k].y, w.y * decay);
+                w.z = fmaf(-c, mv[k].z, w.z * decay);
+                w.w = fmaf(-c, mv[k].w, w.w * decay);
+                wp[idx] = w;
+            }
+        }
+    } else {
+        float mv[VMAX * 4];
+#pragma unroll
+        for (int k = 0; k < VMAX * 4; ++k) {
+            const int idx = k * 256 + tid;
+            if (idx < d.cols) {
+                const float m = fmaf(mu, d.m[base + idx], d.g[base + idx]);
+                d.m[base + idx] = m;
+                mv[k] = m;
+                ss = fmaf(m, m, ss);
+            }
+        }
+        const float tot = block_sum_256(ss, red);
+        const float c = d.coef / max_keep_nan(sqrtf(tot), args.eps);
+        const float decay = args.decay;
+#pragma unroll
+        for (int k = 0; k < VMAX * 4; ++k) {
+            const int idx = k * 256 + tid;
+            if (idx < d.cols) d.w[base + idx] = fmaf(-c, mv[k], d.w[base + idx] * decay);
+        }
+    }
+}
+
+// Rows longer than the register budget: M' is written, then re-read for the update.
+__global__ __launch_bounds__(256) void k_rownorm_rows_long(RowArgs args) {
+    __shared__ float red[4];
+    const int t = blockIdx.x;
+    int gi = 0;
+    while (gi + 1 < args.n && t >= args.d[gi + 1].row_begin) ++gi;
+    const RowDesc& d = args.d[gi];
+    const int row = t - d.row_begin;
+    const int64_t base = (int64_t)row * d.cols;
+    float ss = 0.f;
+    for (int idx = threadIdx.x; idx < d.cols; idx += 256) {
+        const float m = fmaf(args.mu, d.m[base + idx], d.g[base + idx]);
+        d.m[base + idx] = m;
+        ss = fmaf(m, m, ss);
+    }
+    // each thread re-reads only the elements it wrote itself, so no fence is needed
+    const float tot = block_sum_256(ss, red);
+    const float c = d.coef / max_keep_nan(sqrtf(tot), args.eps);
+    for (int idx = threadIdx.x; idx < d.cols; idx += 256)
+        d.w[base + idx] = fmaf(-c, d.m[base + idx], d.w[base + idx] * args.decay);
+}
+
+hipError_t launch_rownorm_rows(const RowArgs& a, int max_cols, bool vec, hipStream_t s) {
+    const dim3 grid(a.total), block(256);
+    if (max_cols > kRowMaxRegisterCols) {
+        hipLaunchKernelGGL(k_rownorm_rows_long, grid, block, 0, s, a);
+    } else if (vec) {
+        const int need = (max_cols + 1023) / 1024;  // float4 per thread
+        if (need <= 2) hipLaunchKernelGGL((k_rownorm_rows<2, true>), grid, block, 0, s, a);
+        else if (need <= 4) hipLaunchKernelGGL((k_rownorm_rows<4, true>), grid, block, 0, s, a);
+        else if (need <= 8) hipLaunchKernelGGL((k_rownorm_rows<8, true>), grid, block, 0, s, a);
+        else if (need <= 12) hipLaunchKernelGGL((k_rownorm_rows<12, true>), grid, block, 0, s, a);
+        else if (need <= 16) hipLaunchKernelGGL((k_rownorm_rows<16, true>), grid, block, 0, s, a);
+        else if (need <= 20) hipLaunchKernelGGL((k_rownorm_rows<20, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_rownorm_rows<32, true>), grid, block, 0, s, a);
+    } else {
+        const int need = (max_cols + 1023) / 1024;
+        if (need <= 2) hipLaunchKernelGGL((k_rownorm_rows<2, false>), grid, block, 0, s, a);
+        else if (need <= 8) hipLaunchKernelGGL((k_rownorm_rows<8, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL(k_rownorm_rows_long, grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------ colnorm (tall) ------
+// Block tile: kColChunkRows rows x kColTileCols columns. Thread layout: 64 lanes
+// cover 256 consecutive columns (one float4 each), the 4 waves interleave rows.
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_colnorm_partial(ColArgs args) {
+    __shared__ float red[4][kColTileCols];
+    const int t = blockIdx.x;
+    const int gi = find_group(args.d, args.n, t);
+    const ColDesc& d = args.d[gi];
+    const int local = t - d.tile_begin;
+    const int chunk = local / d.tiles_c, tcol = local - chunk * d.tiles_c;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c0 = tcol * kColTileCols + lane * 4;
+    const int r0 = chunk * kColChunkRows;
+    const int r1 = min(r0 + kColChunkRows, d.rows);
+    const float mu = args.mu;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    if (VEC && c0 + 3 < d.cols) {
+        for (int r = r0 + wave; r < r1; r += 4) {
+            const int64_t o = (int64_t)r * d.cols + c0;
+            float4 m = *reinterpret_cast<const float4*>(d.m + o);
+            const float4 g = *reinterpret_cast<const float4*>(d.g + o);
+            m.x = fmaf(mu, m.x, g.x);
+            m.y = fmaf(mu, m.y, g.y);
+            m.z = fmaf(mu, m.z, g.z);
+            m.w = fmaf(mu, m.w, g.w);
+            *reinterpret_cast<float4*>(d.m + o) = m;
+            s0 = fmaf(m.x, m.x, s0);
+            s1 = fmaf(m.y, m.y, s1);
+            s2 = fmaf(m.z, m.z, s2);
+            s3 = fmaf(m.w, m.w, s3);
+        }
+    } else {
+        float sv[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int r = r0 + wave; r < r1; r += 4) {
+            const int64_t o = (int64_t)r * d.cols;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = c0 + e;
+                if (c < d.cols) {
+                    const float m = fmaf(mu, d.m[o + c], d.g[o + c]);
+                    d.m[o + c] = m;
+                    sv[e] = fmaf(m, m, sv[e]);
+                }
+            }
+        }
+        s0 = sv[0]; s1 = sv[1]; s2 = sv[2]; s3 = sv[3];
+    }
+    red[wave][lane * 4 + 0] = s0;
+    red[wave][lane * 4 + 1] = s1;
+    red[wave][lane * 4 + 2] = s2;
+    red[wave][lane * 4 + 3] = s3;
+    __syncthreads();
+    const int c = tcol * kColTileCols + tid;
+    if (c < d.cols)
+        d.partial[(int64_t)chunk * d.cols + c] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+}
+
+__global__ __launch_bounds__(256) void k_colnorm_finalize(ColArgs args) {
+    const int t = blockIdx.x;
+    int gi = 0;
+    while (gi + 1 < args.n && t >= args.d[gi + 1].fin_begin) ++gi;
+    const ColDesc& d = args.d[gi];
+    const int c = (t - d.fin_begin) * 256 + threadIdx.x;
+    if (c >= d.cols) return;
+    float s = 0.f;
+    for (int k = 0; k < d.chunks; ++k) s += d.partial[(int64_t)k * d.cols + c];
+    d.inv[c] = 1.0f / max_keep_nan(sqrtf(s), args.eps);
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void k_colnorm_apply(ColArgs args) {
+    const int t = blockIdx.x;
+    const int gi = find_group(args.d, args.n, t);
+    const ColDesc& d = args.d[gi];
+    const int local = t - d.tile_begin;
+    const int chunk = local / d.tiles_c, tcol = local - chunk * d.tiles_c;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c0 = tcol * kColTileCols + lane * 4;
+    const int r0 = chunk * kColChunkRows;
+    const int r1 = min(r0 + kColChunkRows, d.rows);
+    const float decay = args.decay;
+    if (VEC && c0 + 3 < d.cols) {
+        const float4 iv = *reinterpret_cast<const float4*>(d.inv + c0);
+        const float k0 = d.coef * iv.x, k1 = d.coef * iv.y, k2 = d.coef * iv.z, k3 = d.coef * iv.w;
+        for (int r = r0 + wave; r < r1; r += 4) {
+            const int64_t o = (int64_t)r * d.cols + c0;
+            const float4 m = *reinterpret_cast<const float4*>(d.m + o);
+            float4 w = *reinterpret_cast<const float4*>(d.w + o);
+            w.x = fmaf(-k0, m.x, w.x * decay);
+            w.y = fmaf(-k1, m.y, w.y * decay);
+            w.z = fmaf(-k2, m.z, w.z * decay);
+            w.w = fmaf(-k3, m.w, w.w * decay);
+            *reinterpret_cast<float4*>(d.w + o) = w;
+        }
+    } else {
+        float kc[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kc[e] = (c0 + e < d.cols) ? d.coef * d.inv[c0 + e] : 0.f;
+        for (int r = r0 + wave; r < r1; r += 4) {
+            const int64_t o = (int64_t)r * d.cols;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = c0 + e;
+                if (c < d.cols) d.w[o + c] = fmaf(-kc[e], d.m[o + c], d.w[o + c] * decay);
+            }
+        }
+    }
+}
+
+hipError_t launch_colnorm_partial(const ColArgs& a, bool vec, hipStream_t s) {
+    if (vec) hipLaunchKernelGGL(k_colnorm_partial<true>, dim3(a.total), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_colnorm_partial<false>, dim3(a.total), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_colnorm_finalize(const ColArgs& a, int fin_total, hipStream_t s) {
+    hipLaunchKernelGGL(k_colnorm_finalize, dim3(fin_total), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_colnorm_apply(const ColArgs& a, bool vec, hipStream_t s) {
+    if (vec) hipLaunchKernelGGL(k_colnorm_apply<true>, dim3(a.total), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_colnorm_apply<false>, dim3(a.total), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace muon

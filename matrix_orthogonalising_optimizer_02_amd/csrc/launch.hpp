@@ -1,0 +1,137 @@
+// Kernel descriptors and host-side launchers (internal to libmuon_rocm.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace muon {
+
+// ---- momentum + Frobenius partials + bf16 working copies ------------------------
+// One 64x64 tile per block over the padded [rows_p, cols_p] extent of M [rows, cols].
+// `direct` receives bf16(M') in M's orientation ([rows_p, cols_p]); `transp` the
+// transpose ([cols_p, rows_p]). Flat matrices: direct = X_r, transp = X_c; tall
+// matrices: direct = X_c, transp = X_r. Padding is written as zeros.
+struct CastDesc {
+    const float* m_in;
+    const float* g;        // unused when the launch has use_momentum == 0
+    float* m_out;          // M' written here when non-null (may equal m_in)
+    unsigned short* direct;
+    unsigned short* transp;
+    float* partial;        // one float per tile: sum of M'^2 over the tile
+    int32_t rows, cols, rows_p, cols_p;
+    int32_t tiles_c;       // cols_p / 64
+    int32_t tile_begin;    // first tile of this matrix in the launch
+};
+
+struct CastArgs {
+    CastDesc d[kMaxGroup];
+    int32_t n;
+    int32_t total;
+    float mu;
+    int32_t use_momentum;
+};
+
+// ---- per-matrix 1 / max(||M||_F, eps) from the tile partials -------------------
+struct FrobArgs {
+    const float* partial[kMaxGroup];
+    float* scale[kMaxGroup];
+    int32_t count[kMaxGroup];
+    int32_t n;
+    float eps;
+};
+
+// ---- NS5 GEMM stages (bf16 MFMA, fp32 accumulation) ----------------------------
+// Working matrix X is [m, n] with m = min(rows, cols), n = max(rows, cols), padded
+// to [m_p, n_p]. X_r is X row-major [m_p, n_p]; X_c is X^T row-major [n_p, m_p].
+enum GemmMode : int {
+    kModeGram = 0,     // A = s2 * X X^T                  (symmetric tiles)
+    kModePoly = 1,     // B = b A + c A A                  (symmetric tiles)
+    kModeApply = 2,    // X' = s1 * (a X + B X)            bf16 X'_r and X'_c
+    kModeFinalO = 3,   // O  = s1 * (a X + B X)            fp32, input orientation
+    kModeFinalW = 4,   // W <- decay W - upd_coef O        fused Eq. 4 update
+};
+
+struct NsDesc {
+    const unsigned short* xr;
+    const unsigned short* xc;
+    unsigned short* xr_next;
+    unsigned short* xc_next;
+    unsigned short* a;
+    unsigned short* b;
+    float* out;            // O or W: [rows, cols] row-major in the input orientation
+    const float* scale;    // device scalar s = 1 / max(||M||_F, eps)
+    int32_t m, n, m_p, n_p;
+    int32_t tall;
+    int32_t tile_begin;
+    int32_t tiles;         // symmetric: tiles per side; rectangular: tiles along n
+    float upd_coef;        // lr * rms_scale * sqrt(n)
+};
+
+struct NsArgs {
+    NsDesc d[kMaxGroup];
+    int32_t n;
+    int32_t total;
+    float ca, cb, cc;
+    float decay;           // 1 - lr * weight_decay
+    int32_t first;         // first iteration: fold s into the epilogues
+};
+
+// ---- RowNorm step ---------------------------------------------------------------
+struct RowDesc {
+    const float* g;
+    float* m;
+    float* w;
+    int32_t rows, cols;
+    int32_t row_begin;     // first block of this matrix in the launch
+    float coef;            // lr * rms_scale * gamma * sqrt(max(rows, cols))
+};
+
+struct RowArgs {
+    RowDesc d[kMaxGroup];
+    int32_t n;
+    int32_t total;
+    float mu, decay, eps;
+};
+
+struct ColDesc {
+    const float* g;
+    float* m;
+    float* w;
+    float* partial;        // [chunks, cols] per-chunk column sums of M'^2
+    float* inv;            // [cols] 1 / max(column norm, eps)
+    int32_t rows, cols;
+    int32_t chunks;        // ceil(rows / kColChunkRows)
+    int32_t tiles_c;       // ceil(cols / 256)
+    int32_t tile_begin;    // first block of this matrix in the launch
+    int32_t fin_begin;     // first block of this matrix in the finalize launch
+    float coef;
+};
+
+struct ColArgs {
+    ColDesc d[kMaxGroup];
+    int32_t n;
+    int32_t total;
+    float mu, decay, eps;
+};
+
+constexpr int kColChunkRows = 256;
+constexpr int kColTileCols = 256;
+// Rows up to this length keep M' in registers (one 256-thread block per row).
+constexpr int kRowMaxRegisterCols = 32 * 1024;
+
+// Launchers return hipSuccess or the launch error.
+hipError_t launch_cast(const CastArgs& a, hipStream_t s);
+hipError_t launch_frob(const FrobArgs& a, hipStream_t s);
+hipError_t launch_ns_gemm(GemmMode mode, const NsArgs& a, hipStream_t s);
+hipError_t launch_rownorm_rows(const RowArgs& a, int max_cols, bool vec, hipStream_t s);
+hipError_t launch_colnorm_partial(const ColArgs& a, bool vec, hipStream_t s);
+hipError_t launch_colnorm_finalize(const ColArgs& a, int fin_total, hipStream_t s);
+hipError_t launch_colnorm_apply(const ColArgs& a, bool vec, hipStream_t s);
+
+// GEMM tile sizes used by launch_ns_gemm (for the host-side tile counting).
+constexpr int kGemmBM = 128;
+constexpr int kGemmBN = 128;
+
+}  // namespace muon

@@ -1,0 +1,611 @@
+// C ABI of libmuon_rocm: argument validation, bucket planning, workspace layout,
+// kernel dispatch and optional per-kernel timing. Declared in include/muon_rocm.h.
+//
+// Step structure (Muon notes Sec. 2.1 Eq. 1-2, Sec. 2.2 Eq. 4; DiT paper, Periodic
+// Row-wise paragraphs):
+//   refresh step:  cast (M <- mu M + G, ||M||^2 partials, bf16 X_r / X_c)
+//                  -> frob (s = 1 / max(||M||_F, eps))
+//                  -> N x [gram, poly, apply]; the last apply applies Eq. 4 to W
+//   RowNorm step:  rows kernel (flat / square) or partial -> finalize -> apply (tall)
+// Matrices are planned in groups of up to kMaxGroup, ordered by working size m and
+// then by n (largest first), and each group's kernels cover all of its matrices in
+// one launch per stage. Groups run one after another on the caller's stream and
+// reuse the same workspace region.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/muon_rocm.h"
+#include "launch.hpp"
+
+#define MUON_API extern "C" __attribute__((visibility("default")))
+
+namespace muon {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& what) {
+    g_last_error = what;
+    return code;
+}
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int kMaxNsSteps = 100;
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------- planning ----
+struct MatPlan {
+    int idx;                  // caller's index
+    int64_t rows, cols;
+    bool tall;                // rows > cols
+    int64_t m, n, m_p, n_p;   // working dims and padded dims
+    int64_t rows_p, cols_p;   // padded dims in the input orientation
+    int64_t cast_tiles;
+    // workspace offsets (relative to the group base)
+    size_t xr[2], xc[2], a, b, partial, scale;  // refresh
+    size_t colpart, inv;                        // RowNorm, tall only
+    int64_t chunks;
+};
+
+struct GroupPlan {
+    std::vector<MatPlan> mats;
+    size_t bytes = 0;
+};
+
+struct Plan {
+    std::vector<GroupPlan> groups;
+    size_t bytes = 0;
+};
+
+int make_plan(const int64_t* rows, const int64_t* cols, int32_t count, Plan* plan) {
+    std::vector<MatPlan> all;
+    for (int i = 0; i < count; ++i) {
+        const int64_t r = rows[i], c = cols[i];
+        if (r < 0 || c < 0) return fail(MUON_ERR_INVALID_ARG, "negative matrix dimension at index " + std::to_string(i));
+        if (r == 0 || c == 0) continue;
+        if (r > kMaxDim || c > kMaxDim || r * c > kMaxElems)
+            return fail(MUON_ERR_TOO_LARGE, "matrix " + std::to_string(i) + " exceeds the size limits");
+        MatPlan p{};
+        p.idx = i;
+        p.rows = r;
+        p.cols = c;
+        p.tall = r > c;
+        p.m = std::min(r, c);
+        p.n = std::max(r, c);
+        p.m_p = round_up(p.m, kPad);
+        p.n_p = round_up(p.n, kPad);
+        p.rows_p = p.tall ? p.n_p : p.m_p;
+        p.cols_p = p.tall ? p.m_p : p.n_p;
+        p.cast_tiles = (p.rows_p / 64) * (p.cols_p / 64);
+        p.chunks = (r + kColChunkRows - 1) / kColChunkRows;
+        all.push_back(p);
+    }
+    std::stable_sort(all.begin(), all.end(), [](const MatPlan& x, const MatPlan& y) {
+        if (x.m != y.m) return x.m > y.m;
+        return x.n > y.n;
+    });
+    plan->groups.clear();
+    plan->bytes = 0;
+    for (size_t s = 0; s < all.size(); s += kMaxGroup) {
+        GroupPlan gp;
+        size_t ns = 0, rn = 0;
+        int64_t cast_total = 0, rows_total = 0, col_total = 0;
+        for (size_t k = s; k < std::min(all.size(), s + kMaxGroup); ++k) {
+            MatPlan p = all[k];
+            const size_t xbytes = size_t(p.m_p) * size_t(p.n_p) * 2;
+            const size_t abytes = size_t(p.m_p) * size_t(p.m_p) * 2;
+            for (int q = 0; q < 2; ++q) { p.xr[q] = ns; ns = align256(ns + xbytes); }
+            for (int q = 0; q < 2; ++q) { p.xc[q] = ns; ns = align256(ns + xbytes); }
+            p.a = ns; ns = align256(ns + abytes);
+            p.b = ns; ns = align256(ns + abytes);
+            p.partial = ns; ns = align256(ns + size_t(p.cast_tiles) * 4);
+            p.scale = ns; ns = align256(ns + 4);
+            if (p.tall) {
+                p.colpart = rn; rn = align256(rn + size_t(p.chunks) * size_t(p.cols) * 4);
+                p.inv = rn; rn = align256(rn + size_t(p.cols) * 4);
+                col_total += p.chunks * ((p.cols + kColTileCols - 1) / kColTileCols);
+            } else {
+                rows_total += p.rows;
+            }
+            cast_total += p.cast_tiles;
+            gp.mats.push_back(p);
+        }
+        const int64_t tile_total_cap = int64_t(1) << 31;
+        if (cast_total >= tile_total_cap || rows_total >= tile_total_cap || col_total >= tile_total_cap)
+            return fail(MUON_ERR_TOO_LARGE, "a launch would exceed 2^31 workgroups");
+        gp.bytes = std::max(ns, rn);
+        plan->bytes = std::max(plan->bytes, gp.bytes);
+        plan->groups.push_back(std::move(gp));
+    }
+    return MUON_OK;
+}
+
+// ---------------------------------------------------------------- timing ----
+struct TimingRecord {
+    int cls;
+    hipEvent_t start, stop;
+};
+
+struct Timing {
+    std::mutex mu;
+    bool enabled = false;
+    std::vector<TimingRecord> records;
+    std::vector<hipEvent_t> pool;
+} g_timing;
+
+hipEvent_t take_event() {
+    if (!g_timing.pool.empty()) {
+        hipEvent_t e = g_timing.pool.back();
+        g_timing.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+template <class F>
+int run_kernel(int cls, hipStream_t s, const char* name, F&& launch) {
+    hipEvent_t a = nullptr, b = nullptr;
+    bool timed = false;
+    {
+        std::lock_guard<std::mutex> lk(g_timing.mu);
+        if (g_timing.enabled) {
+            a = take_event();
+            b = take_event();
+            timed = a && b;
+            if (timed && hipEventRecord(a, s) != hipSuccess) timed = false;
+        }
+    }
+    const hipError_t e = launch();
+    if (e != hipSuccess) return fail(MUON_ERR_HIP, std::string(name) + ": " + hipGetErrorString(e));
+    if (timed) {
+        std::lock_guard<std::mutex> lk(g_timing.mu);
+        if (hipEventRecord(b, s) == hipSuccess) g_timing.records.push_back({cls, a, b});
+    }
+    return MUON_OK;
+}
+
+// ---------------------------------------------------------------- checks ----
+int check_hparams(const muon_hparams* hp, bool need_steps) {
+    if (!hp) return fail(MUON_ERR_INVALID_ARG, "hparams is NULL");
+    if (!(hp->eps > 0.f) || !std::isfinite(hp->eps)) return fail(MUON_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (hp->ns_steps < 1 || hp->ns_steps > kMaxNsSteps)
+        return fail(MUON_ERR_INVALID_ARG, "ns_steps must be in [1, 100]");
+    if (need_steps && hp->period_k < 1) return fail(MUON_ERR_INVALID_ARG, "period_k must be >= 1");
+    return MUON_OK;
+}
+
+struct Range {
+    uintptr_t lo, hi;
+    bool write;
+};
+
+int check_overlaps(std::vector<Range>& rs) {
+    std::sort(rs.begin(), rs.end(), [](const Range& x, const Range& y) { return x.lo < y.lo; });
+    uintptr_t hi_any = 0, hi_write = 0;
+    for (const Range& r : rs) {
+        if (r.hi <= r.lo) continue;
+        if (r.lo < (r.write ? hi_any : hi_write)) return fail(MUON_ERR_ALIAS, "buffers overlap");
+        hi_any = std::max(hi_any, r.hi);
+        if (r.write) hi_write = std::max(hi_write, r.hi);
+    }
+    return MUON_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int check_workspace(const Plan& plan, void* ws, size_t ws_bytes, std::vector<Range>& ranges) {
+    if (plan.bytes == 0) return MUON_OK;
+    if (!ws) return fail(MUON_ERR_WORKSPACE, "workspace is NULL");
+    if (ws_bytes < plan.bytes)
+        return fail(MUON_ERR_WORKSPACE, "workspace too small: need " + std::to_string(plan.bytes) + " bytes");
+    if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(MUON_ERR_ALIGN, "workspace not 256-byte aligned");
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(ws);
+    ranges.push_back({lo, lo + plan.bytes, true});
+    return MUON_OK;
+}
+
+int check_matrices(const muon_matrix* mats, int32_t count, std::vector<int64_t>& rows,
+                   std::vector<int64_t>& cols, std::vector<Range>& ranges) {
+    if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count < 0");
+    if (count > 0 && !mats) return fail(MUON_ERR_INVALID_ARG, "mats is NULL");
+    rows.resize(count);
+    cols.resize(count);
+    for (int i = 0; i < count; ++i) {
+        const muon_matrix& t = mats[i];
+        rows[i] = t.rows;
+        cols[i] = t.cols;
+        if (t.rows < 0 || t.cols < 0) return fail(MUON_ERR_INVALID_ARG, "negative dimension at index " + std::to_string(i));
+        if (t.rows == 0 || t.cols == 0) continue;
+        if (t.rows > kMaxDim || t.cols > kMaxDim || t.rows * t.cols > kMaxElems)
+            return fail(MUON_ERR_TOO_LARGE, "matrix " + std::to_string(i) + " exceeds the size limits");
+        if (!t.w || !t.m || !t.g) return fail(MUON_ERR_INVALID_ARG, "NULL w, m or g at index " + std::to_string(i));
+        if (!aligned16(t.w) || !aligned16(t.m) || !aligned16(t.g))
+            return fail(MUON_ERR_ALIGN, "matrix pointer not 16-byte aligned at index " + std::to_string(i));
+        const uintptr_t bytes = uintptr_t(t.rows) * uintptr_t(t.cols) * 4;
+        ranges.push_back({reinterpret_cast<uintptr_t>(t.w), reinterpret_cast<uintptr_t>(t.w) + bytes, true});
+        ranges.push_back({reinterpret_cast<uintptr_t>(t.m), reinterpret_cast<uintptr_t>(t.m) + bytes, true});
+        ranges.push_back({reinterpret_cast<uintptr_t>(t.g), reinterpret_cast<uintptr_t>(t.g) + bytes, false});
+    }
+    return MUON_OK;
+}
+
+// ---------------------------------------------------------------- dispatch ----
+struct IoPtrs {
+    const float* m_in;
+    const float* g;
+    float* m_out;
+    float* out;  // W (fused update) or O
+};
+
+int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_hparams& hp,
+                bool momentum, bool update_w, char* ws, hipStream_t s) {
+    const int ng = int(gp.mats.size());
+    // cast
+    CastArgs ca{};
+    ca.n = ng;
+    ca.mu = hp.mu;
+    ca.use_momentum = momentum ? 1 : 0;
+    int64_t tiles = 0;
+    for (int k = 0; k < ng; ++k) {
+        const MatPlan& p = gp.mats[k];
+        CastDesc& d = ca.d[k];
+        d.m_in = io[k].m_in;
+        d.g = io[k].g;
+        d.m_out = io[k].m_out;
+        unsigned short* xr = reinterpret_cast<unsigned short*>(ws + p.xr[0]);
+        unsigned short* xc = reinterpret_cast<unsigned short*>(ws + p.xc[0]);
+        d.direct = p.tall ? xc : xr;
+        d.transp = p.tall ? xr : xc;
+        d.partial = reinterpret_cast<float*>(ws + p.partial);
+        d.rows = int32_t(p.rows);
+        d.cols = int32_t(p.cols);
+        d.rows_p = int32_t(p.rows_p);
+        d.cols_p = int32_t(p.cols_p);
+        d.tiles_c = int32_t(p.cols_p / 64);
+        d.tile_begin = int32_t(tiles);
+        tiles += p.cast_tiles;
+    }
+    ca.total = int32_t(tiles);
+    int rc = run_kernel(MUON_KCLASS_CAST, s, "cast", [&] { return launch_cast(ca, s); });
+    if (rc) return rc;
+
+    FrobArgs fa{};
+    fa.n = ng;
+    fa.eps = hp.eps;
+    for (int k = 0; k < ng; ++k) {
+        const MatPlan& p = gp.mats[k];
+        fa.partial[k] = reinterpret_cast<const float*>(ws + p.partial);
+        fa.scale[k] = reinterpret_cast<float*>(ws + p.scale);
+        fa.count[k] = int32_t(p.cast_tiles);
+    }
+    rc = run_kernel(MUON_KCLASS_FROB, s, "frob", [&] { return launch_frob(fa, s); });
+    if (rc) return rc;
+
+    NsArgs na{};
+    na.n = ng;
+    na.ca = hp.ns_a;
+    na.cb = hp.ns_b;
+    na.cc = hp.ns_c;
+    na.decay = 1.0f - hp.lr * hp.weight_decay;
+    for (int it = 0; it < hp.ns_steps; ++it) {
+        const int cur = it & 1, nxt = cur ^ 1;
+        na.first = it == 0 ? 1 : 0;
+        for (int k = 0; k < ng; ++k) {
+            const MatPlan& p = gp.mats[k];
+            NsDesc& d = na.d[k];
+            d.xr = reinterpret_cast<const unsigned short*>(ws + p.xr[cur]);
+            d.xc = reinterpret_cast<const unsigned short*>(ws + p.xc[cur]);
+            d.xr_next = reinterpret_cast<unsigned short*>(ws + p.xr[nxt]);
+            d.xc_next = reinterpret_cast<unsigned short*>(ws + p.xc[nxt]);
+            d.a = reinterpret_cast<unsigned short*>(ws + p.a);
+            d.b = reinterpret_cast<unsigned short*>(ws + p.b);
+            d.out = io[k].out;
+            d.scale = reinterpret_cast<const float*>(ws + p.scale);
+            d.m = int32_t(p.m);
+            d.n = int32_t(p.n);
+            d.m_p = int32_t(p.m_p);
+            d.n_p = int32_t(p.n_p);
+            d.tall = p.tall ? 1 : 0;
+            d.upd_coef = float(double(hp.lr) * double(hp.rms_scale) * std::sqrt(double(p.n)));
+        }
+        // symmetric stages: upper-triangular tiles
+        int64_t tot = 0;
+        for (int k = 0; k < ng; ++k) {
+            const int64_t t = gp.mats[k].m_p / kGemmBM;
+            na.d[k].tiles = int32_t(t);
+            na.d[k].tile_begin = int32_t(tot);
+            tot += t * (t + 1) / 2;
+        }
+        na.total = int32_t(tot);
+        rc = run_kernel(MUON_KCLASS_GRAM, s, "gram", [&] { return launch_ns_gemm(kModeGram, na, s); });
+        if (rc) return rc;
+        rc = run_kernel(MUON_KCLASS_POLY, s, "poly", [&] { return launch_ns_gemm(kModePoly, na, s); });
+        if (rc) return rc;
+        // apply: full rectangle [m_p / BM] x [n_p / BN]
+        tot = 0;
+        for (int k = 0; k < ng; ++k) {
+            const MatPlan& p = gp.mats[k];
+            na.d[k].tiles = int32_t(p.n_p / kGemmBN);
+            na.d[k].tile_begin = int32_t(tot);
+            tot += (p.m_p / kGemmBM) * (p.n_p / kGemmBN);
+        }
+        na.total = int32_t(tot);
+        const bool last = it + 1 == hp.ns_steps;
+        const GemmMode mode = !last ? kModeApply : (update_w ? kModeFinalW : kModeFinalO);
+        rc = run_kernel(last ? MUON_KCLASS_APPLY_FINAL : MUON_KCLASS_APPLY, s, "apply",
+                        [&] { return launch_ns_gemm(mode, na, s); });
+        if (rc) return rc;
+    }
+    return MUON_OK;
+}
+
+int run_rownorm(const GroupPlan& gp, const muon_matrix* mats, const muon_hparams& hp, char* ws,
+                hipStream_t s) {
+    const float decay = 1.0f - hp.lr * hp.weight_decay;
+    RowArgs ra{};
+    ra.mu = hp.mu;
+    ra.decay = decay;
+    ra.eps = hp.eps;
+    ColArgs ca{};
+    ca.mu = hp.mu;
+    ca.decay = decay;
+    ca.eps = hp.eps;
+    int64_t rows_total = 0, col_total = 0, fin_total = 0;
+    int max_cols = 0;
+    bool row_vec = true, col_vec = true;
+    for (const MatPlan& p : gp.mats) {
+        const muon_matrix& t = mats[p.idx];
+        const float coef = float(double(hp.lr) * double(hp.rms_scale) * double(hp.gamma) * std::sqrt(double(p.n)));
+        if (!p.tall) {
+            RowDesc& d = ra.d[ra.n++];
+            d.g = t.g;
+            d.m = t.m;
+            d.w = t.w;
+            d.rows = int32_t(p.rows);
+            d.cols = int32_t(p.cols);
+            d.row_begin = int32_t(rows_total);
+            d.coef = coef;
+            rows_total += p.rows;
+            max_cols = std::max<int>(max_cols, int(p.cols));
+            row_vec = row_vec && (p.cols % 4 == 0);
+        } else {
+            ColDesc& d = ca.d[ca.n++];
+            d.g = t.g;
+            d.m = t.m;
+            d.w = t.w;
+            d.partial = reinterpret_cast<float*>(ws + p.colpart);
+            d.inv = reinterpret_cast<float*>(ws + p.inv);
+            d.rows = int32_t(p.rows);
+            d.cols = int32_t(p.cols);
+            d.chunks = int32_t(p.chunks);
+            d.tiles_c = int32_t((p.cols + kColTileCols - 1) / kColTileCols);
+            d.tile_begin = int32_t(col_total);
+            d.fin_begin = int32_t(fin_total);
+            d.coef = coef;
+            col_total += int64_t(d.chunks) * d.tiles_c;
+            fin_total += (p.cols + 255) / 256;
+            col_vec = col_vec && (p.cols % 4 == 0);
+        }
+    }
+    int rc = MUON_OK;
+    if (ra.n > 0) {
+        ra.total = int32_t(rows_total);
+        rc = run_kernel(MUON_KCLASS_ROWNORM_ROWS, s, "rownorm_rows",
+                        [&] { return launch_rownorm_rows(ra, max_cols, row_vec, s); });
+        if (rc) return rc;
+    }
+    if (ca.n > 0) {
+        ca.total = int32_t(col_total);
+        rc = run_kernel(MUON_KCLASS_COLNORM_PARTIAL, s, "colnorm_partial",
+                        [&] { return launch_colnorm_partial(ca, col_vec, s); });
+        if (rc) return rc;
+        rc = run_kernel(MUON_KCLASS_COLNORM_FINALIZE, s, "colnorm_finalize",
+                        [&] { return launch_colnorm_finalize(ca, int(fin_total), s); });
+        if (rc) return rc;
+        rc = run_kernel(MUON_KCLASS_COLNORM_APPLY, s, "colnorm_apply",
+                        [&] { return launch_colnorm_apply(ca, col_vec, s); });
+    }
+    return rc;
+}
+
+int do_rownorm(const muon_matrix* mats, int32_t count, const muon_hparams* hp, void* ws,
+               size_t ws_bytes, void* stream, bool need_k) {
+    g_last_error.clear();
+    int rc = check_hparams(hp, need_k);
+    if (rc) return rc;
+    std::vector<int64_t> rows, cols;
+    std::vector<Range> ranges;
+    rc = check_matrices(mats, count, rows, cols, ranges);
+    if (rc) return rc;
+    Plan plan;
+    rc = make_plan(rows.data(), cols.data(), count, &plan);
+    if (rc) return rc;
+    rc = check_workspace(plan, ws, ws_bytes, ranges);
+    if (rc) return rc;
+    rc = check_overlaps(ranges);
+    if (rc) return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    for (const GroupPlan& gp : plan.groups) {
+        rc = run_rownorm(gp, mats, *hp, static_cast<char*>(ws), s);
+        if (rc) return rc;
+    }
+    return MUON_OK;
+}
+
+}  // namespace
+}  // namespace muon
+
+using namespace muon;
+
+MUON_API int muon_abi_version(void) { return MUON_ABI_VERSION; }
+
+MUON_API const char* muon_status_str(int status) {
+    switch (status) {
+        case MUON_OK: return "ok";
+        case MUON_ERR_INVALID_ARG: return "invalid argument";
+        case MUON_ERR_WORKSPACE: return "workspace missing or too small";
+        case MUON_ERR_ALIGN: return "misaligned pointer";
+        case MUON_ERR_ALIAS: return "overlapping buffers";
+        case MUON_ERR_HIP: return "HIP runtime error";
+        case MUON_ERR_TOO_LARGE: return "problem too large";
+        default: return "unknown status";
+    }
+}
+
+MUON_API const char* muon_last_error(void) { return g_last_error.c_str(); }
+
+MUON_API void muon_default_hparams(muon_hparams* hp) {
+    if (!hp) return;
+    hp->lr = 1e-3f;
+    hp->weight_decay = 0.1f;
+    hp->mu = 0.95f;
+    hp->ns_a = 3.4445f;
+    hp->ns_b = -4.7750f;
+    hp->ns_c = 2.0315f;
+    hp->rms_scale = 0.2f;
+    hp->gamma = 0.15f;
+    hp->eps = 1e-7f;
+    hp->ns_steps = 5;
+    hp->period_k = 3;
+}
+
+MUON_API int muon_workspace_bytes(const int64_t* rows, const int64_t* cols, int32_t count, size_t* bytes) {
+    g_last_error.clear();
+    if (!bytes) return fail(MUON_ERR_INVALID_ARG, "bytes is NULL");
+    if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count < 0");
+    if (count > 0 && (!rows || !cols)) return fail(MUON_ERR_INVALID_ARG, "rows or cols is NULL");
+    Plan plan;
+    const int rc = make_plan(rows, cols, count, &plan);
+    if (rc) return rc;
+    *bytes = plan.bytes;
+    return MUON_OK;
+}
+
+MUON_API int muon_step(const muon_matrix* mats, int32_t count, const muon_hparams* hp, int64_t step,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    if (step < 0) return fail(MUON_ERR_INVALID_ARG, "step < 0");
+    int rc = check_hparams(hp, true);
+    if (rc) return rc;
+    if (step % hp->period_k != 0)
+        return do_rownorm(mats, count, hp, workspace, workspace_bytes, stream, true);
+    std::vector<int64_t> rows, cols;
+    std::vector<Range> ranges;
+    rc = check_matrices(mats, count, rows, cols, ranges);
+    if (rc) return rc;
+    Plan plan;
+    rc = make_plan(rows.data(), cols.data(), count, &plan);
+    if (rc) return rc;
+    rc = check_workspace(plan, workspace, workspace_bytes, ranges);
+    if (rc) return rc;
+    rc = check_overlaps(ranges);
+    if (rc) return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    for (const GroupPlan& gp : plan.groups) {
+        std::vector<IoPtrs> io;
+        for (const MatPlan& p : gp.mats) {
+            const muon_matrix& t = mats[p.idx];
+            io.push_back({t.m, t.g, t.m, t.w});
+        }
+        rc = run_refresh(gp, io, *hp, true, true, static_cast<char*>(workspace), s);
+        if (rc) return rc;
+    }
+    return MUON_OK;
+}
+
+MUON_API int ns5_batched(const float* const* m_in, float* const* o_out, const int64_t* rows,
+                         const int64_t* cols, int32_t count, const muon_hparams* hp, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    int rc = check_hparams(hp, false);
+    if (rc) return rc;
+    if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count < 0");
+    if (count > 0 && (!m_in || !o_out || !rows || !cols))
+        return fail(MUON_ERR_INVALID_ARG, "NULL array argument");
+    std::vector<Range> ranges;
+    for (int i = 0; i < count; ++i) {
+        if (rows[i] < 0 || cols[i] < 0) return fail(MUON_ERR_INVALID_ARG, "negative dimension at index " + std::to_string(i));
+        if (rows[i] == 0 || cols[i] == 0) continue;
+        if (rows[i] > kMaxDim || cols[i] > kMaxDim || rows[i] * cols[i] > kMaxElems)
+            return fail(MUON_ERR_TOO_LARGE, "matrix " + std::to_string(i) + " exceeds the size limits");
+        if (!m_in[i] || !o_out[i]) return fail(MUON_ERR_INVALID_ARG, "NULL matrix pointer at index " + std::to_string(i));
+        if (!aligned16(m_in[i]) || !aligned16(o_out[i]))
+            return fail(MUON_ERR_ALIGN, "matrix pointer not 16-byte aligned at index " + std::to_string(i));
+        const uintptr_t bytes = uintptr_t(rows[i]) * uintptr_t(cols[i]) * 4;
+        const uintptr_t pi = reinterpret_cast<uintptr_t>(m_in[i]), po = reinterpret_cast<uintptr_t>(o_out[i]);
+        if (pi == po) {
+            ranges.push_back({po, po + bytes, true});
+        } else {
+            ranges.push_back({pi, pi + bytes, false});
+            ranges.push_back({po, po + bytes, true});
+        }
+    }
+    Plan plan;
+    rc = make_plan(rows, cols, count, &plan);
+    if (rc) return rc;
+    rc = check_workspace(plan, workspace, workspace_bytes, ranges);
+    if (rc) return rc;
+    rc = check_overlaps(ranges);
+    if (rc) return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    for (const GroupPlan& gp : plan.groups) {
+        std::vector<IoPtrs> io;
+        for (const MatPlan& p : gp.mats) io.push_back({m_in[p.idx], nullptr, nullptr, o_out[p.idx]});
+        rc = run_refresh(gp, io, *hp, false, false, static_cast<char*>(workspace), s);
+        if (rc) return rc;
+    }
+    return MUON_OK;
+}
+
+MUON_API int rownorm_update(const muon_matrix* mats, int32_t count, const muon_hparams* hp,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    return do_rownorm(mats, count, hp, workspace, workspace_bytes, stream, false);
+}
+
+MUON_API int muon_timing_enable(int enable) {
+    g_last_error.clear();
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (!enable) {
+        for (TimingRecord& r : g_timing.records) {
+            g_timing.pool.push_back(r.start);
+            g_timing.pool.push_back(r.stop);
+        }
+        g_timing.records.clear();
+    }
+    g_timing.enabled = enable != 0;
+    return MUON_OK;
+}
+
+MUON_API int muon_timing_read(double* ms, int64_t* launches) {
+    g_last_error.clear();
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    int rc = MUON_OK;
+    for (TimingRecord& r : g_timing.records) {
+        float t = 0.f;
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, r.start, r.stop);
+        if (e != hipSuccess) {
+            rc = fail(MUON_ERR_HIP, std::string("timing: ") + hipGetErrorString(e));
+        } else if (r.cls >= 0 && r.cls < MUON_KCLASS_COUNT) {
+            if (ms) ms[r.cls] += double(t);
+            if (launches) launches[r.cls] += 1;
+        }
+        g_timing.pool.push_back(r.start);
+        g_timing.pool.push_back(r.stop);
+    }
+    g_timing.records.clear();
+    return rc;
+}
