@@ -24,6 +24,9 @@ COMMON_FLAGS = [
     f"--offload-arch={ARCH}",
     # packed fp32 VALU ops stay off: scalar fp32 code is what the kernels are written for
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the GEMM epilogues index the accumulator array with loop variables; they must
+    # unroll completely or the accumulators end up in scratch memory
+    "-mllvm", "-pragma-unroll-threshold=1000000",
 ]
 
 
@@ -34,9 +37,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libmuon_rocm.so")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile all sources and link the shared library; returns its path."""
+def build(verbose: bool = False, defines=(), out: str = LIB_PATH) -> str:
+    """Compile all sources and link the shared library; returns its path.
+
+    `defines` are extra -D options (tile-configuration constants); `out` places the
+    library elsewhere, e.g. to compare configurations side by side.
+    """
     cc = hipcc()
+    dflags = [f"-D{d}" for d in defines]
     tmp = tempfile.mkdtemp(prefix="muon_build_")
     try:
         objs = []
@@ -44,15 +52,15 @@ def build(verbose: bool = False) -> str:
             path = os.path.join(CSRC, src)
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmd = [cc, *COMMON_FLAGS, *lang, "-c", path, "-o", obj]
+            cmd = [cc, *COMMON_FLAGS, *dflags, *lang, "-c", path, "-o", obj]
             _run(cmd, verbose)
             objs.append(obj)
-        out_tmp = LIB_PATH + ".tmp"
+        out_tmp = out + ".tmp"
         _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", out_tmp], verbose)
-        os.replace(out_tmp, LIB_PATH)
+        os.replace(out_tmp, out)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB_PATH
+    return out
 
 
 def _run(cmd, verbose):

@@ -124,14 +124,27 @@ constexpr int kRowMaxRegisterCols = 32 * 1024;
 // Launchers return hipSuccess or the launch error.
 hipError_t launch_cast(const CastArgs& a, hipStream_t s);
 hipError_t launch_frob(const FrobArgs& a, hipStream_t s);
-hipError_t launch_ns_gemm(GemmMode mode, const NsArgs& a, hipStream_t s);
+enum GemmTile : int { kTileSmall = 0, kTileBig = 1 };
+hipError_t launch_ns_gemm(GemmMode mode, GemmTile tile, const NsArgs& a, hipStream_t s);
 hipError_t launch_rownorm_rows(const RowArgs& a, int max_cols, bool vec, hipStream_t s);
 hipError_t launch_colnorm_partial(const ColArgs& a, bool vec, hipStream_t s);
 hipError_t launch_colnorm_finalize(const ColArgs& a, int fin_total, hipStream_t s);
 hipError_t launch_colnorm_apply(const ColArgs& a, bool vec, hipStream_t s);
 
-// GEMM tile sizes used by launch_ns_gemm (for the host-side tile counting).
-constexpr int kGemmBM = 128;
-constexpr int kGemmBN = 128;
+// GEMM block tiles (host-side tile counting must match the kernels).
+#ifndef MUON_GEMM_BIG_M
+#define MUON_GEMM_BIG_M 256
+#endif
+#ifndef MUON_GEMM_BIG_N
+#define MUON_GEMM_BIG_N 256
+#endif
+constexpr int kGemmSmall = 128;
+constexpr int kGemmBigM = MUON_GEMM_BIG_M;
+constexpr int kGemmBigN = MUON_GEMM_BIG_N;
+// A stage uses the big tile when it has at least this many big tiles.
+#ifndef MUON_GEMM_BIG_MIN_TILES
+#define MUON_GEMM_BIG_MIN_TILES 512
+#endif
+constexpr int kGemmBigMinTiles = MUON_GEMM_BIG_MIN_TILES;
 
 }  // namespace muon

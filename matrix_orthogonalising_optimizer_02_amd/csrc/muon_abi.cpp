@@ -250,6 +250,42 @@ struct IoPtrs {
     float* out;  // W (fused update) or O
 };
 
+// Fills tiles / tile_begin / total of a GEMM stage launch and returns the tile
+// configuration: the big tile when the stage has at least kGemmBigMinTiles of them
+// (symmetric stages need a square tile), the small one otherwise.
+GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym) {
+    const int ng = int(gp.mats.size());
+    int64_t big = 0;
+    for (int k = 0; k < ng; ++k) {
+        const MatPlan& p = gp.mats[k];
+        if (sym) {
+            const int64_t t = p.m_p / kGemmBigM;
+            big += t * (t + 1) / 2;
+        } else {
+            big += (p.m_p / kGemmBigM) * (p.n_p / kGemmBigN);
+        }
+    }
+    const bool big_ok = !sym || kGemmBigM == kGemmBigN;
+    const GemmTile tile = (big_ok && big >= kGemmBigMinTiles) ? kTileBig : kTileSmall;
+    const int64_t bm = tile == kTileBig ? kGemmBigM : kGemmSmall;
+    const int64_t bn = tile == kTileBig ? kGemmBigN : kGemmSmall;
+    int64_t tot = 0;
+    for (int k = 0; k < ng; ++k) {
+        const MatPlan& p = gp.mats[k];
+        na.d[k].tile_begin = int32_t(tot);
+        if (sym) {
+            const int64_t t = p.m_p / bm;
+            na.d[k].tiles = int32_t(t);
+            tot += t * (t + 1) / 2;
+        } else {
+            na.d[k].tiles = int32_t(p.n_p / bn);
+            tot += (p.m_p / bm) * (p.n_p / bn);
+        }
+    }
+    na.total = int32_t(tot);
+    return tile;
+}
+
 int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_hparams& hp,
                 bool momentum, bool update_w, char* ws, hipStream_t s) {
     const int ng = int(gp.mats.size());
@@ -321,32 +357,16 @@ int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_h
             d.tall = p.tall ? 1 : 0;
             d.upd_coef = float(double(hp.lr) * double(hp.rms_scale) * std::sqrt(double(p.n)));
         }
-        // symmetric stages: upper-triangular tiles
-        int64_t tot = 0;
-        for (int k = 0; k < ng; ++k) {
-            const int64_t t = gp.mats[k].m_p / kGemmBM;
-            na.d[k].tiles = int32_t(t);
-            na.d[k].tile_begin = int32_t(tot);
-            tot += t * (t + 1) / 2;
-        }
-        na.total = int32_t(tot);
-        rc = run_kernel(MUON_KCLASS_GRAM, s, "gram", [&] { return launch_ns_gemm(kModeGram, na, s); });
+        const GemmTile sym_tile = plan_tiles(gp, na, true);
+        rc = run_kernel(MUON_KCLASS_GRAM, s, "gram", [&] { return launch_ns_gemm(kModeGram, sym_tile, na, s); });
         if (rc) return rc;
-        rc = run_kernel(MUON_KCLASS_POLY, s, "poly", [&] { return launch_ns_gemm(kModePoly, na, s); });
+        rc = run_kernel(MUON_KCLASS_POLY, s, "poly", [&] { return launch_ns_gemm(kModePoly, sym_tile, na, s); });
         if (rc) return rc;
-        // apply: full rectangle [m_p / BM] x [n_p / BN]
-        tot = 0;
-        for (int k = 0; k < ng; ++k) {
-            const MatPlan& p = gp.mats[k];
-            na.d[k].tiles = int32_t(p.n_p / kGemmBN);
-            na.d[k].tile_begin = int32_t(tot);
-            tot += (p.m_p / kGemmBM) * (p.n_p / kGemmBN);
-        }
-        na.total = int32_t(tot);
+        const GemmTile apply_tile = plan_tiles(gp, na, false);
         const bool last = it + 1 == hp.ns_steps;
         const GemmMode mode = !last ? kModeApply : (update_w ? kModeFinalW : kModeFinalO);
         rc = run_kernel(last ? MUON_KCLASS_APPLY_FINAL : MUON_KCLASS_APPLY, s, "apply",
-                        [&] { return launch_ns_gemm(mode, na, s); });
+                        [&] { return launch_ns_gemm(mode, apply_tile, na, s); });
         if (rc) return rc;
     }
     return MUON_OK;
