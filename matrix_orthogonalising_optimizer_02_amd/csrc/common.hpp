@@ -58,12 +58,4 @@ __device__ __forceinline__ float block_sum_256(float v, float* red /* >= 4 float
     return s;
 }
 
-// Map a block index to a logical work index so that each XCD (blocks are dealt
-// round-robin over the 8 XCDs) receives one contiguous range of logical indices;
-// neighbouring tiles then share operands in the same L2.
-__device__ __forceinline__ int xcd_remap(int b, int total) {
-    const int q = total >> 3, r = total & 7, x = b & 7, loc = b >> 3;
-    return x * q + (x < r ? x : r) + loc;
-}
-
 }  // namespace muon

@@ -56,7 +56,14 @@ struct GemmCfg {
     static constexpr int LB = BN * CPR / NT;
     static constexpr int IA = BM / RPI / 4;       // 1 KiB loads per wave per stage (direct path)
     static constexpr int IB = BN / RPI / 4;
-    static constexpr int kLdsBytes = STAGES * (BM + BN) * BK * 2;
+    // epilogue staging, per wave and per half of its columns (HN of them): a bf16
+    // transposed tile [HN][WM + 8] plus a bf16 direct tile [WM][HN + 8], or one fp32 tile
+    static constexpr int HN = WN / 2;
+    static constexpr int kEpiBf16 = (HN * (WM + 8) + WM * (HN + 8)) * 2;
+    static constexpr int kEpiF32 = (HN * (WM + 4) > WM * (HN + 4) ? HN * (WM + 4) : WM * (HN + 4)) * 4;
+    static constexpr int kEpiWave = ((kEpiBf16 > kEpiF32 ? kEpiBf16 : kEpiF32) + 15) / 16 * 16;
+    static constexpr int kMainBytes = STAGES * (BM + BN) * BK * 2;
+    static constexpr int kLdsBytes = kMainBytes > 4 * kEpiWave ? kMainBytes : 4 * kEpiWave;
     static_assert(BK == 32 || BK == 64, "K step");
     static_assert(kDirect || STAGES == 2, "the register-staged path is double-buffered");
 };
@@ -143,11 +150,28 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
 
-    const int t = xcd_remap(blockIdx.x, args.total);
-    int gi = 0;
-    while (gi + 1 < args.n && t >= args.d[gi + 1].tile_begin) ++gi;
+    // Blocks are dealt round-robin over the 8 XCDs (block b runs on XCD b % 8). Every
+    // XCD walks the group's matrices in order (longest K first) and takes one contiguous
+    // eighth of each matrix's tile sequence: equal work per XCD even when the matrices'
+    // K differ, and neighbouring tiles (shared operand panels) in the same L2. Blocks
+    // left without a tile (the grid is 8 x the largest per-XCD count) exit here.
+    int gi = -1, local = 0;
+    {
+        const int x = blockIdx.x & 7;
+        int sl = blockIdx.x >> 3;
+        for (int g = 0; g < args.n; ++g) {
+            const int T = args.d[g].ntiles;
+            const int lo = (x * T) >> 3, cnt = (((x + 1) * T) >> 3) - lo;
+            if (sl < cnt) {
+                gi = g;
+                local = lo + sl;
+                break;
+            }
+            sl -= cnt;
+        }
+    }
+    if (gi < 0) return;
     const NsDesc& d = args.d[gi];
-    int local = t - d.tile_begin;
 
     constexpr bool kSym = (MODE == kModeGram || MODE == kModePoly);
     int ti, tj;
@@ -361,159 +385,191 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
 
     // ---- epilogue. Accumulator element r of a 32x32 block sits at row
     // 8*(r/4) + 4*(lane/32) + r%4, column lane%32: each lane owns 4 consecutive rows of
-    // one column, which are contiguous in the transposed layouts (X_c, the mirrored
-    // half of A, W of a tall matrix). Every load of a block is issued before the
-    // first use, so the epilogue pays one memory latency, not one per element group.
+    // one column. Results are staged per wave through LDS, half of the wave's columns at
+    // a time, and leave in 16-byte row chunks: the direct orientation C[i][j] and/or the
+    // transposed one C[j][i] (X'_r / X'_c, a symmetric tile and its mirror, or W of a
+    // flat / tall matrix). Operands of the epilogue math (X for a X, the mirrored half
+    // of A for b A) are read where a lane's 4 rows are contiguous.
+    constexpr int HN = Cfg::HN, NBH = TN / 2;     // columns and 32-column blocks per half
+    constexpr int TSB = WM + 8, DSB = HN + 8;     // bf16 strides: transposed, direct
+    constexpr int TSF = WM + 4, DSF = HN + 4;     // fp32 strides
     const float first_s = args.first ? *d.scale : 1.0f;
     const int row_base = ti * BM + wm * WM;
     const int col_base = tj * BN + wn * WN;
     const int lj = lane & 31, li = (lane >> 5) * 4;
+    unsigned short* const lt = sA + wave * (Cfg::kEpiWave / 2);   // transposed staging
+    unsigned short* const ldr = lt + HN * TSB;                      // direct staging
+    float* const lf = reinterpret_cast<float*>(lt);                 // fp32 staging
 
+    constexpr bool kBf16Out = (MODE == kModeGram || MODE == kModePoly || MODE == kModeApply);
+    // outputs of the bf16 modes
+    unsigned short* dst_d = nullptr;  // direct [i][j]
+    unsigned short* dst_t = nullptr;  // transposed [j][i]
+    int64_t ld_d = 0, ld_t = 0;
     if constexpr (MODE == kModeGram || MODE == kModePoly) {
-        unsigned short* C = (MODE == kModeGram) ? d.a : d.b;
-        const int64_t ldc = d.m_p;
-        // b * A[i][j] with A symmetric: read A[j][i0 .. i0+3] (8 contiguous bytes); one
-        // 32-row slab is prefetched ahead of the slab being stored
-        u32x2 av[2][TN][4];
-        auto load_a = [&](int buf, int a) {
+        dst_d = (MODE == kModeGram) ? d.a : d.b;
+        dst_t = (ti != tj) ? dst_d : nullptr;
+        ld_d = ld_t = d.m_p;
+    } else if constexpr (MODE == kModeApply) {
+        dst_d = d.xr_next;
+        dst_t = d.xc_next;
+        ld_d = d.n_p;
+        ld_t = d.m_p;
+    }
+    const float g2 = first_s * first_s;
+
 #pragma unroll
-            for (int b = 0; b < TN; ++b)
+    for (int h = 0; h < 2; ++h) {
+        // operands of the epilogue math for this half: 8 contiguous bytes per (a, b, rg)
+        u32x2 opv[TM][NBH][4];
+        if constexpr (MODE != kModeGram) {
+            const unsigned short* src = (MODE == kModePoly) ? d.a : d.xc;
+            const int64_t lds = d.m_p;  // A is [m_p, m_p]; X_c is [n_p, m_p]
 #pragma unroll
-                for (int rg = 0; rg < 4; ++rg)
-                    av[buf][b][rg] = *reinterpret_cast<const u32x2*>(
-                        d.a + (int64_t)(col_base + b * 32 + lj) * ldc + row_base + a * 32 + rg * 8 + li);
-        };
-        if constexpr (MODE == kModePoly) load_a(0, 0);
-        const float g2 = first_s * first_s;
+            for (int a = 0; a < TM; ++a)
+#pragma unroll
+                for (int bb = 0; bb < NBH; ++bb)
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg)
+                        opv[a][bb][rg] = *reinterpret_cast<const u32x2*>(
+                            src + (int64_t)(col_base + (h * NBH + bb) * 32 + lj) * lds + row_base + a * 32 + rg * 8 + li);
+        }
+        // values -> LDS
 #pragma unroll
         for (int a = 0; a < TM; ++a) {
-            if constexpr (MODE == kModePoly) {
-                if (a + 1 < TM) load_a((a + 1) & 1, a + 1);
-            }
 #pragma unroll
-            for (int b = 0; b < TN; ++b) {
-                const int j = col_base + b * 32 + lj;
+            for (int bb = 0; bb < NBH; ++bb) {
+                const int b = h * NBH + bb;
+                const int jl = bb * 32 + lj;  // column within the half
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
-                    const int i0 = row_base + a * 32 + rg * 8 + li;
-                    unsigned short h[4];
+                    const int il = a * 32 + rg * 8 + li;  // first of 4 rows within the wave tile
+                    float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         float x = acc[a][b][rg * 4 + e];
                         if constexpr (MODE == kModeGram) {
                             x *= g2;
                         } else {
-                            const u32x2 w = av[a & 1][b][rg];
+                            const u32x2 w = opv[a][bb][rg];
                             const unsigned w32 = (e < 2) ? w.x : w.y;
-                            const float aij = bf2f((unsigned short)((e & 1) ? (w32 >> 16) : (w32 & 0xffff)));
-                            x = fmaf(args.cb, aij, args.cc * x);
+                            const float o = bf2f((unsigned short)((e & 1) ? (w32 >> 16) : (w32 & 0xffff)));
+                            if constexpr (MODE == kModePoly) x = fmaf(args.cb, o, args.cc * x);
+                            else x = fmaf(args.ca, o, x) * first_s;
                         }
-                        h[e] = f2bf(x);
-                        C[(int64_t)(i0 + e) * ldc + j] = h[e];
+                        v[e] = x;
                     }
-                    if (ti != tj) {
+                    if constexpr (kBf16Out) {
+                        unsigned short hv[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) hv[e] = f2bf(v[e]);
                         u32x2 pk;
-                        pk.x = pack2(h[0], h[1]);
-                        pk.y = pack2(h[2], h[3]);
-                        *reinterpret_cast<u32x2*>(C + (int64_t)j * ldc + i0) = pk;
+                        pk.x = pack2(hv[0], hv[1]);
+                        pk.y = pack2(hv[2], hv[3]);
+                        *reinterpret_cast<u32x2*>(lt + jl * TSB + il) = pk;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ldr[(il + e) * DSB + jl] = hv[e];
+                    } else if (d.tall) {
+                        floatx4 o;
+                        o.x = v[0]; o.y = v[1]; o.z = v[2]; o.w = v[3];
+                        *reinterpret_cast<floatx4*>(lf + jl * TSF + il) = o;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) lf[(il + e) * DSF + jl] = v[e];
                     }
                 }
             }
         }
-    } else {
-        // a X[i][j] from X_c[j][i0 .. i0+3]; one 32-row slab is prefetched ahead
-        u32x2 xv[2][TN][4];
-        auto load_x = [&](int buf, int a) {
+        wait_lgkm0();  // this wave's staging writes are complete before its lanes read them
+        const int colh = col_base + h * HN;  // first global column of this half
+        if constexpr (kBf16Out) {
+            // transposed rows: HN rows of WM values (WM / 8 chunks each)
+            if (dst_t) {
 #pragma unroll
-            for (int b = 0; b < TN; ++b)
+                for (int it = 0; it < HN * WM / 8 / 64; ++it) {
+                    const int c = it * 64 + lane, r = c / (WM / 8), k = c % (WM / 8);
+                    const u32x4 val = *reinterpret_cast<const u32x4*>(lt + r * TSB + k * 8);
+                    *reinterpret_cast<u32x4*>(dst_t + (int64_t)(colh + r) * ld_t + row_base + k * 8) = val;
+                }
+            }
+            // direct rows: WM rows of HN values (HN / 8 chunks each)
 #pragma unroll
-                for (int rg = 0; rg < 4; ++rg)
-                    xv[buf][b][rg] = *reinterpret_cast<const u32x2*>(
-                        d.xc + (int64_t)(col_base + b * 32 + lj) * d.m_p + row_base + a * 32 + rg * 8 + li);
-        };
-        load_x(0, 0);
-#pragma unroll
-        for (int a = 0; a < TM; ++a) {
-            if (a + 1 < TM) load_x((a + 1) & 1, a + 1);
-            // final modes: the W values of this 32-row slab are fetched before use
-            float wv[TN][4][4];
+            for (int it = 0; it < WM * HN / 8 / 64; ++it) {
+                const int c = it * 64 + lane, r = c / (HN / 8), k = c % (HN / 8);
+                const u32x4 val = *reinterpret_cast<const u32x4*>(ldr + r * DSB + k * 8);
+                *reinterpret_cast<u32x4*>(dst_d + (int64_t)(row_base + r) * ld_d + colh + k * 8) = val;
+            }
+        } else if (d.tall) {
+            // O / W is [n, m]: row j holds WM consecutive i of this tile (WM / 4 chunks)
+            constexpr int CH = WM / 4, N = HN * CH / 64;
+            floatx4 wv[N];
             if constexpr (MODE == kModeFinalW) {
 #pragma unroll
-                for (int b = 0; b < TN; ++b) {
-                    const int j = col_base + b * 32 + lj;
+                for (int it = 0; it < N; ++it) {
+                    const int c = it * 64 + lane, r = c / CH, k = c % CH;
+                    const int j = colh + r, i = row_base + k * 4;
+                    if (j < d.n && ((d.m & 3) == 0) && i + 3 < d.m)
+                        wv[it] = *reinterpret_cast<const floatx4*>(d.out + (int64_t)j * d.m + i);
+                    else
 #pragma unroll
-                    for (int rg = 0; rg < 4; ++rg) {
-                        const int i0 = row_base + a * 32 + rg * 8 + li;
-                        if (!d.tall) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                wv[b][rg][e] = (i0 + e < d.m && j < d.n) ? d.out[(int64_t)(i0 + e) * d.n + j] : 0.f;
-                        } else if (j < d.n && ((d.m & 3) == 0) && i0 + 3 < d.m) {
-                            const floatx4 w4 = *reinterpret_cast<const floatx4*>(d.out + (int64_t)j * d.m + i0);
-                            wv[b][rg][0] = w4.x; wv[b][rg][1] = w4.y; wv[b][rg][2] = w4.z; wv[b][rg][3] = w4.w;
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                wv[b][rg][e] = (i0 + e < d.m && j < d.n) ? d.out[(int64_t)j * d.m + i0 + e] : 0.f;
-                        }
-                    }
+                        for (int e = 0; e < 4; ++e)
+                            wv[it][e] = (j < d.n && i + e < d.m) ? d.out[(int64_t)j * d.m + i + e] : 0.f;
                 }
             }
 #pragma unroll
-            for (int b = 0; b < TN; ++b) {
-                const int j = col_base + b * 32 + lj;
+            for (int it = 0; it < N; ++it) {
+                const int c = it * 64 + lane, r = c / CH, k = c % CH;
+                const int j = colh + r, i = row_base + k * 4;
+                floatx4 o = *reinterpret_cast<const floatx4*>(lf + r * TSF + k * 4);
+                if constexpr (MODE == kModeFinalW) {
 #pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const int i0 = row_base + a * 32 + rg * 8 + li;
-                    float v[4];
+                    for (int e = 0; e < 4; ++e) o[e] = fmaf(-d.upd_coef, o[e], wv[it][e] * args.decay);
+                }
+                if (j < d.n && ((d.m & 3) == 0) && i + 3 < d.m) {
+                    *reinterpret_cast<floatx4*>(d.out + (int64_t)j * d.m + i) = o;
+                } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const u32x2 xw = xv[a & 1][b][rg];
-                        const unsigned w32 = (e < 2) ? xw.x : xw.y;
-                        const float x = bf2f((unsigned short)((e & 1) ? (w32 >> 16) : (w32 & 0xffff)));
-                        v[e] = fmaf(args.ca, x, acc[a][b][rg * 4 + e]) * first_s;
-                    }
-                    if constexpr (MODE == kModeApply) {
-                        unsigned short h[4];
+                    for (int e = 0; e < 4; ++e)
+                        if (j < d.n && i + e < d.m) d.out[(int64_t)j * d.m + i + e] = o[e];
+                }
+            }
+        } else {
+            // O / W is [m, n]: row i holds HN consecutive j of this half (HN / 4 chunks)
+            constexpr int CH = HN / 4, N = WM * CH / 64;
+            floatx4 wv[N];
+            if constexpr (MODE == kModeFinalW) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            h[e] = f2bf(v[e]);
-                            d.xr_next[(int64_t)(i0 + e) * d.n_p + j] = h[e];
-                        }
-                        u32x2 pk;
-                        pk.x = pack2(h[0], h[1]);
-                        pk.y = pack2(h[2], h[3]);
-                        *reinterpret_cast<u32x2*>(d.xc_next + (int64_t)j * d.m_p + i0) = pk;
-                    } else {
-                        float r[4];
+                for (int it = 0; it < N; ++it) {
+                    const int c = it * 64 + lane, r = c / CH, k = c % CH;
+                    const int i = row_base + r, j = colh + k * 4;
+                    if (i < d.m && ((d.n & 3) == 0) && j + 3 < d.n)
+                        wv[it] = *reinterpret_cast<const floatx4*>(d.out + (int64_t)i * d.n + j);
+                    else
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            if constexpr (MODE == kModeFinalO) r[e] = v[e];
-                            else r[e] = fmaf(-d.upd_coef, v[e], wv[b][rg][e] * args.decay);
-                        }
-                        // O, or the Eq. 4 update of W, in the input orientation
-                        if (!d.tall) {
-                            if (j < d.n) {
+                        for (int e = 0; e < 4; ++e)
+                            wv[it][e] = (i < d.m && j + e < d.n) ? d.out[(int64_t)i * d.n + j + e] : 0.f;
+                }
+            }
 #pragma unroll
-                                for (int e = 0; e < 4; ++e)
-                                    if (i0 + e < d.m) d.out[(int64_t)(i0 + e) * d.n + j] = r[e];
-                            }
-                        } else if (j < d.n) {
-                            float* rowp = d.out + (int64_t)j * d.m;
-                            if (((d.m & 3) == 0) && i0 + 3 < d.m) {
-                                floatx4 o;
-                                o.x = r[0]; o.y = r[1]; o.z = r[2]; o.w = r[3];
-                                *reinterpret_cast<floatx4*>(rowp + i0) = o;
-                            } else {
+            for (int it = 0; it < N; ++it) {
+                const int c = it * 64 + lane, r = c / CH, k = c % CH;
+                const int i = row_base + r, j = colh + k * 4;
+                floatx4 o = *reinterpret_cast<const floatx4*>(lf + r * DSF + k * 4);
+                if constexpr (MODE == kModeFinalW) {
 #pragma unroll
-                                for (int e = 0; e < 4; ++e)
-                                    if (i0 + e < d.m) rowp[i0 + e] = r[e];
-                            }
-                        }
-                    }
+                    for (int e = 0; e < 4; ++e) o[e] = fmaf(-d.upd_coef, o[e], wv[it][e] * args.decay);
+                }
+                if (i < d.m && ((d.n & 3) == 0) && j + 3 < d.n) {
+                    *reinterpret_cast<floatx4*>(d.out + (int64_t)i * d.n + j) = o;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (i < d.m && j + e < d.n) d.out[(int64_t)i * d.n + j + e] = o[e];
                 }
             }
         }
+        // the next half overwrites the staging area: LDS executes a wave's operations in
+        // order, so its writes cannot overtake the reads above
     }
 }
 

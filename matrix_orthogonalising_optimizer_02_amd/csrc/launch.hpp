@@ -64,7 +64,7 @@ struct NsDesc {
     const float* scale;    // device scalar s = 1 / max(||M||_F, eps)
     int32_t m, n, m_p, n_p;
     int32_t tall;
-    int32_t tile_begin;
+    int32_t ntiles;        // tiles of this matrix in the stage
     int32_t tiles;         // symmetric: tiles per side; rectangular: tiles along n
     float upd_coef;        // lr * rms_scale * sqrt(n)
 };
@@ -72,7 +72,7 @@ struct NsDesc {
 struct NsArgs {
     NsDesc d[kMaxGroup];
     int32_t n;
-    int32_t total;
+    int32_t total;         // grid size: 8 x the largest per-XCD tile count
     float ca, cb, cc;
     float decay;           // 1 - lr * weight_decay
     int32_t first;         // first iteration: fold s into the epilogues

@@ -269,19 +269,28 @@ GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym) {
     const GemmTile tile = (big_ok && big >= kGemmBigMinTiles) ? kTileBig : kTileSmall;
     const int64_t bm = tile == kTileBig ? kGemmBigM : kGemmSmall;
     const int64_t bn = tile == kTileBig ? kGemmBigN : kGemmSmall;
-    int64_t tot = 0;
     for (int k = 0; k < ng; ++k) {
         const MatPlan& p = gp.mats[k];
-        na.d[k].tile_begin = int32_t(tot);
         if (sym) {
             const int64_t t = p.m_p / bm;
             na.d[k].tiles = int32_t(t);
-            tot += t * (t + 1) / 2;
+            na.d[k].ntiles = int32_t(t * (t + 1) / 2);
         } else {
             na.d[k].tiles = int32_t(p.n_p / bn);
-            tot += (p.m_p / bm) * (p.n_p / bn);
+            na.d[k].ntiles = int32_t((p.m_p / bm) * (p.n_p / bn));
         }
     }
+    // the kernels deal each matrix's tiles over the 8 XCDs in contiguous eighths
+    int64_t per_xcd_max = 0;
+    for (int x = 0; x < 8; ++x) {
+        int64_t c = 0;
+        for (int k = 0; k < ng; ++k) {
+            const int64_t T = na.d[k].ntiles;
+            c += ((x + 1) * T >> 3) - (x * T >> 3);
+        }
+        per_xcd_max = std::max(per_xcd_max, c);
+    }
+    const int64_t tot = 8 * per_xcd_max;
     na.total = int32_t(tot);
     return tile;
 }
