@@ -33,52 +33,67 @@ __global__ __launch_bounds__(256) void k_cast(CastArgs args) {
     const bool vec = (d.cols & 3) == 0;
     const bool mom = args.use_momentum != 0;
     const float mu = args.mu;
+    // All loads of the tile are issued before the first store: M' is stored through
+    // one pointer and M / G read through others, so a store could otherwise keep the
+    // compiler from moving the following loads ahead of it.
+    float vv[4][4];
+    if (vec) {
+        floatx4 mm[4], gg[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = tr * 64 + rq + 16 * q;
+            const bool ok = r < d.rows && c0 + 3 < d.cols;
+            const int64_t o = (int64_t)r * d.cols + c0;
+            mm[q] = ok ? *reinterpret_cast<const floatx4*>(d.m_in + o) : floatx4{0.f, 0.f, 0.f, 0.f};
+            gg[q] = (ok && mom) ? *reinterpret_cast<const floatx4*>(d.g + o) : floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = tr * 64 + rq + 16 * q;
+            const bool ok = r < d.rows && c0 + 3 < d.cols;
+            floatx4 m = mm[q];
+            if (mom) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m[e] = fmaf(mu, m[e], gg[q][e]);
+            }
+            if (ok && d.m_out) *reinterpret_cast<floatx4*>(d.m_out + (int64_t)r * d.cols + c0) = m;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vv[q][e] = m[e];
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = tr * 64 + rq + 16 * q;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = c0 + e;
+                float x = 0.f;
+                if (r < d.rows && c < d.cols) {
+                    const int64_t o = (int64_t)r * d.cols + c;
+                    x = d.m_in[o];
+                    if (mom) x = fmaf(mu, x, d.g[o]);
+                    if (d.m_out) d.m_out[o] = x;
+                }
+                vv[q][e] = x;
+            }
+        }
+    }
     float ss = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int rl = rq + 16 * q;
         const int r = tr * 64 + rl;
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
-        if (r < d.rows) {
-            const int64_t base = (int64_t)r * d.cols;
-            if (vec && c0 + 3 < d.cols) {
-                float4 mm = *reinterpret_cast<const float4*>(d.m_in + base + c0);
-                if (mom) {
-                    const float4 gg = *reinterpret_cast<const float4*>(d.g + base + c0);
-                    mm.x = fmaf(mu, mm.x, gg.x);
-                    mm.y = fmaf(mu, mm.y, gg.y);
-                    mm.z = fmaf(mu, mm.z, gg.z);
-                    mm.w = fmaf(mu, mm.w, gg.w);
-                }
-                if (d.m_out) *reinterpret_cast<float4*>(d.m_out + base + c0) = mm;
-                v[0] = mm.x; v[1] = mm.y; v[2] = mm.z; v[3] = mm.w;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int c = c0 + e;
-                    if (c < d.cols) {
-                        float x = d.m_in[base + c];
-                        if (mom) x = fmaf(mu, x, d.g[base + c]);
-                        if (d.m_out) d.m_out[base + c] = x;
-                        v[e] = x;
-                    }
-                }
-            }
-        }
-        ss = fmaf(v[0], v[0], ss);
-        ss = fmaf(v[1], v[1], ss);
-        ss = fmaf(v[2], v[2], ss);
-        ss = fmaf(v[3], v[3], ss);
         unsigned short h[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            h[e] = f2bf(v[e]);
+            ss = fmaf(vv[q][e], vv[q][e], ss);
+            h[e] = f2bf(vv[q][e]);
             tile[rl][c4 * 4 + e] = h[e];
         }
-        uint2 packed;
+        u32x2 packed;
         packed.x = pack2(h[0], h[1]);
         packed.y = pack2(h[2], h[3]);
-        *reinterpret_cast<uint2*>(d.direct + (int64_t)r * d.cols_p + c0) = packed;
+        *reinterpret_cast<u32x2*>(d.direct + (int64_t)r * d.cols_p + c0) = packed;
     }
     __syncthreads();
     {
@@ -88,8 +103,11 @@ __global__ __launch_bounds__(256) void k_cast(CastArgs args) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) w8[e] = pack2(tile[ob + 2 * e][oc], tile[ob + 2 * e + 1][oc]);
         unsigned short* dst = d.transp + (int64_t)(tc * 64 + oc) * d.rows_p + tr * 64 + ob;
-        reinterpret_cast<uint4*>(dst)[0] = make_uint4(w8[0], w8[1], w8[2], w8[3]);
-        reinterpret_cast<uint4*>(dst)[1] = make_uint4(w8[4], w8[5], w8[6], w8[7]);
+        u32x4 lo, hi;
+        lo.x = w8[0]; lo.y = w8[1]; lo.z = w8[2]; lo.w = w8[3];
+        hi.x = w8[4]; hi.y = w8[5]; hi.z = w8[6]; hi.w = w8[7];
+        reinterpret_cast<u32x4*>(dst)[0] = lo;
+        reinterpret_cast<u32x4*>(dst)[1] = hi;
     }
     const float s = block_sum_256(ss, red);
     if (tid == 0) d.partial[local] = s;
@@ -140,42 +158,58 @@ __global__ __launch_bounds__(256) void k_rownorm_rows(RowArgs args) {
     const float mu = args.mu;
     float ss = 0.f;
     if constexpr (VEC) {
-        float4 mv[VMAX];
-        const float4* gp = reinterpret_cast<const float4*>(d.g + base);
-        float4* mp = reinterpret_cast<float4*>(d.m + base);
-        float4* wp = reinterpret_cast<float4*>(d.w + base);
+        // Loads are issued in batches of kB float4 ahead of the batch's stores (M' is
+        // written through a pointer that the compiler cannot prove distinct from G's).
+        constexpr int kB = 4;
+        floatx4 mv[VMAX];
+        const floatx4* gp = reinterpret_cast<const floatx4*>(d.g + base);
+        floatx4* mp = reinterpret_cast<floatx4*>(d.m + base);
+        floatx4* wp = reinterpret_cast<floatx4*>(d.w + base);
         const int nv = d.cols >> 2;
 #pragma unroll
-        for (int k = 0; k < VMAX; ++k) {
-            const int idx = k * 256 + tid;
-            if (idx < nv) {
-                float4 m = mp[idx];
-                const float4 g = gp[idx];
-                m.x = fmaf(mu, m.x, g.x);
-                m.y = fmaf(mu, m.y, g.y);
-                m.z = fmaf(mu, m.z, g.z);
-                m.w = fmaf(mu, m.w, g.w);
-                mp[idx] = m;
-                mv[k] = m;
-                ss = fmaf(m.x, m.x, ss);
-                ss = fmaf(m.y, m.y, ss);
-                ss = fmaf(m.z, m.z, ss);
-                ss = fmaf(m.w, m.w, ss);
+        for (int k0 = 0; k0 < VMAX; k0 += kB) {
+            floatx4 gv[kB];
+#pragma unroll
+            for (int k = k0; k < k0 + kB && k < VMAX; ++k) {
+                const int idx = k * 256 + tid;
+                if (idx < nv) {
+                    mv[k] = mp[idx];
+                    gv[k - k0] = gp[idx];
+                }
+            }
+#pragma unroll
+            for (int k = k0; k < k0 + kB && k < VMAX; ++k) {
+                const int idx = k * 256 + tid;
+                if (idx < nv) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        mv[k][e] = fmaf(mu, mv[k][e], gv[k - k0][e]);
+                        ss = fmaf(mv[k][e], mv[k][e], ss);
+                    }
+                    mp[idx] = mv[k];
+                }
             }
         }
         const float tot = block_sum_256(ss, red);
         const float c = d.coef / max_keep_nan(sqrtf(tot), args.eps);
         const float decay = args.decay;
 #pragma unroll
-        for (int k = 0; k < VMAX; ++k) {
-            const int idx = k * 256 + tid;
-            if (idx < nv) {
-                float4 w = wp[idx];
-                w.x = fmaf(-c, mv[k].x, w.x * decay);
-                w.y = fmaf(-c, mv[k].y, w.y * decay);
-                w.z = fmaf(-c, mv[k].z, w.z * decay);
-                w.w = fmaf(-c, mv[k].w, w.w * decay);
-                wp[idx] = w;
+        for (int k0 = 0; k0 < VMAX; k0 += kB) {
+            floatx4 wv[kB];
+#pragma unroll
+            for (int k = k0; k < k0 + kB && k < VMAX; ++k) {
+                const int idx = k * 256 + tid;
+                if (idx < nv) wv[k - k0] = wp[idx];
+            }
+#pragma unroll
+            for (int k = k0; k < k0 + kB && k < VMAX; ++k) {
+                const int idx = k * 256 + tid;
+                if (idx < nv) {
+                    floatx4 w = wv[k - k0];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = fmaf(-c, mv[k][e], w[e] * decay);
+                    wp[idx] = w;
+                }
             }
         }
     } else {
@@ -263,19 +297,33 @@ __global__ __launch_bounds__(256) void k_colnorm_partial(ColArgs args) {
     const float mu = args.mu;
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
     if (VEC && c0 + 3 < d.cols) {
-        for (int r = r0 + wave; r < r1; r += 4) {
-            const int64_t o = (int64_t)r * d.cols + c0;
-            float4 m = *reinterpret_cast<const float4*>(d.m + o);
-            const float4 g = *reinterpret_cast<const float4*>(d.g + o);
-            m.x = fmaf(mu, m.x, g.x);
-            m.y = fmaf(mu, m.y, g.y);
-            m.z = fmaf(mu, m.z, g.z);
-            m.w = fmaf(mu, m.w, g.w);
-            *reinterpret_cast<float4*>(d.m + o) = m;
-            s0 = fmaf(m.x, m.x, s0);
-            s1 = fmaf(m.y, m.y, s1);
-            s2 = fmaf(m.z, m.z, s2);
-            s3 = fmaf(m.w, m.w, s3);
+        // rows in batches of kB, loads ahead of stores
+        constexpr int kB = 8;
+        for (int rb = r0 + wave; rb < r1; rb += 4 * kB) {
+            floatx4 mv[kB], gv[kB];
+#pragma unroll
+            for (int q = 0; q < kB; ++q) {
+                const int r = rb + 4 * q;
+                if (r < r1) {
+                    const int64_t o = (int64_t)r * d.cols + c0;
+                    mv[q] = *reinterpret_cast<const floatx4*>(d.m + o);
+                    gv[q] = *reinterpret_cast<const floatx4*>(d.g + o);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < kB; ++q) {
+                const int r = rb + 4 * q;
+                if (r < r1) {
+                    floatx4 m = mv[q];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) m[e] = fmaf(mu, m[e], gv[q][e]);
+                    *reinterpret_cast<floatx4*>(d.m + (int64_t)r * d.cols + c0) = m;
+                    s0 = fmaf(m[0], m[0], s0);
+                    s1 = fmaf(m[1], m[1], s1);
+                    s2 = fmaf(m[2], m[2], s2);
+                    s3 = fmaf(m[3], m[3], s3);
+                }
+            }
         }
     } else {
         float sv[4] = {0.f, 0.f, 0.f, 0.f};
@@ -328,17 +376,32 @@ __global__ __launch_bounds__(256) void k_colnorm_apply(ColArgs args) {
     const int r1 = min(r0 + kColChunkRows, d.rows);
     const float decay = args.decay;
     if (VEC && c0 + 3 < d.cols) {
-        const float4 iv = *reinterpret_cast<const float4*>(d.inv + c0);
-        const float k0 = d.coef * iv.x, k1 = d.coef * iv.y, k2 = d.coef * iv.z, k3 = d.coef * iv.w;
-        for (int r = r0 + wave; r < r1; r += 4) {
-            const int64_t o = (int64_t)r * d.cols + c0;
-            const float4 m = *reinterpret_cast<const float4*>(d.m + o);
-            float4 w = *reinterpret_cast<const float4*>(d.w + o);
-            w.x = fmaf(-k0, m.x, w.x * decay);
-            w.y = fmaf(-k1, m.y, w.y * decay);
-            w.z = fmaf(-k2, m.z, w.z * decay);
-            w.w = fmaf(-k3, m.w, w.w * decay);
-            *reinterpret_cast<float4*>(d.w + o) = w;
+        const floatx4 iv = *reinterpret_cast<const floatx4*>(d.inv + c0);
+        floatx4 kc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kc[e] = d.coef * iv[e];
+        constexpr int kB = 8;
+        for (int rb = r0 + wave; rb < r1; rb += 4 * kB) {
+            floatx4 mv[kB], wv[kB];
+#pragma unroll
+            for (int q = 0; q < kB; ++q) {
+                const int r = rb + 4 * q;
+                if (r < r1) {
+                    const int64_t o = (int64_t)r * d.cols + c0;
+                    mv[q] = *reinterpret_cast<const floatx4*>(d.m + o);
+                    wv[q] = *reinterpret_cast<const floatx4*>(d.w + o);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < kB; ++q) {
+                const int r = rb + 4 * q;
+                if (r < r1) {
+                    floatx4 w = wv[q];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[e] = fmaf(-kc[e], mv[q][e], w[e] * decay);
+                    *reinterpret_cast<floatx4*>(d.w + (int64_t)r * d.cols + c0) = w;
+                }
+            }
         }
     } else {
         float kc[4];
