@@ -43,6 +43,30 @@ def apply_flops(m, n):
     return 2.0 * m * m * n
 
 
+def measured_traffic(kernel, workload_key):
+    """HBM bytes per dispatch of `kernel` from the committed rocprofv3 counter summary.
+
+    The summary records FETCH_SIZE / WRITE_SIZE per dispatch, the copy-kernel
+    calibration factors and a hash of the GEMM sources; a changed kernel (or another
+    workload) gets None, as counters taken on other code say nothing about it.
+    """
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_15b_h5120.json")
+    if workload_key != "15b" or not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    h = hashlib.sha256()
+    for src in rec["gemm_sources"]:
+        with open(os.path.join(ROOT, "matrix_orthogonalising_optimizer_02_amd", "csrc", src), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != rec["gemm_source_sha256"]:
+        return None
+    entry = rec["kernels"].get(kernel)
+    return None if entry is None else entry["hbm_bytes_per_dispatch"]
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,7 +268,8 @@ def main():
         "rownorm_frac_of_hbm_peak": round(rn_gbs / PEAK_HBM_GBS, 4),
         "roofline": {"bound": "mfma", "kernel": "k_ns_gemm<apply> (B X, iterations 1..4)",
                      "achieved": round(apply_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(apply_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(apply_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("k_ns_gemm<2, muon::GemmCfg<256, 256, true, 32, 4> >", args.workload),
                      "launch_ms": round(apply_launch_ms, 4), "launch_flops": apply_launch_flops},
         "kernels": kernels,
     }
