@@ -31,6 +31,18 @@ Readings taken where the pages are silent (each is also listed in the design not
       the extracted plain text but is present in its LaTeX form and in Eq. 7).
   R8  Tall matrices (A > B) run Newton-Schulz on M^T so the Gram matrix is the
       smaller one; the result is transposed back. Identical in exact arithmetic.
+  R14 The scale rules of [MS] Sec. 3.1 replace the factor 0.2 * sqrt(max(A, B)) of
+      Eq. 4: Eq. 5 uses 0.2 * sqrt(H) with H the model's hidden size (a caller
+      parameter), Eq. 6 uses 0.2 / RMS(O) with RMS(O) = sqrt(mean(O^2)), divided as
+      max(RMS(O), eps) so that O = 0 gives a zero update (the page divides exactly).
+      Eq. 7 is Eq. 4.
+  R15 On RowNorm steps Eq. 6 takes RMS(R) = 1/sqrt(max(A, B)), the exact RMS of a
+      RowNorm output whose lines all have norm >= eps, so the step is 0.2 * sqrt(max)
+      * gamma * R as under Eq. 4. (Measuring RMS(gamma R) instead would cancel gamma,
+      which [DiT] uses to set the RowNorm step size relative to NS5.)
+  R16 The update-RMS monitor of a step is RMS(c U): the RMS of the term that Eq. 4
+      (5, 6) multiplies by the learning rate, weight decay excluded; [MS] Lemma 1 and
+      the consistent-update-RMS paragraph make it about 0.2 under Eq. 4.
 
 Parity pins (tests/test_oracle_pins.py): every function here is pinned to a closed
 form, an invariant or a brute-force computation that is not this code.
@@ -63,6 +75,11 @@ class OracleHParams:
     period_k: int = 3
     gamma: float = 0.15
     eps: float = 1e-7
+    scale_mode: str = "max_dim"   # "max_dim" (Eq. 4 / Eq. 7), "hidden" (Eq. 5), "rms" (Eq. 6)
+    hidden: int = 0               # H of Eq. 5
+
+
+SCALE_MODES = ("max_dim", "hidden", "rms")
 
 
 def _f64(x) -> np.ndarray:
@@ -122,6 +139,39 @@ def scaled_update(w, u, lr: float, weight_decay: float, rms_scale: float = 0.2) 
     return w - lr * (rms_scale * _f64(u) * math.sqrt(n) + weight_decay * w)
 
 
+def rms(x) -> float:
+    """RMS(X) = sqrt(mean of the squared entries) ([MS] Lemma 1, Sec. 3.1 Eq. 6)."""
+    x = _f64(x)
+    return math.sqrt(float(np.sum(x * x)) / x.size) if x.size else 0.0
+
+
+def direction_scale(u, shape, kind: str, hp) -> float:
+    """The factor c that multiplies the direction U in W - lr (c U + lambda W).
+
+    kind is "ns5" (U = O on refresh steps) or "rownorm" (U = gamma R).
+      max_dim: c = 0.2 sqrt(max(A, B))       ([MS] Eq. 4, the same as Eq. 7)
+      hidden:  c = 0.2 sqrt(H)               ([MS] Eq. 5)
+      rms:     c = 0.2 / max(RMS(O), eps)    ([MS] Eq. 6, R14) on refresh steps,
+               c = 0.2 sqrt(max(A, B))       on RowNorm steps (R15)
+    """
+    mode = hp.scale_mode
+    if mode not in SCALE_MODES:
+        raise ValueError(f"unknown scale mode {mode!r}")
+    if mode == "hidden":
+        if hp.hidden < 1:
+            raise ValueError("the hidden scale rule needs hidden >= 1")
+        return hp.rms_scale * math.sqrt(hp.hidden)
+    if mode == "rms" and kind == "ns5":
+        return hp.rms_scale / max(rms(u), hp.eps)
+    return hp.rms_scale * math.sqrt(max(shape))
+
+
+def apply_update(w, u, coef: float, lr: float, weight_decay: float) -> np.ndarray:
+    """W_t = W_{t-1} - lr * (coef * U + lambda * W_{t-1}) (the common form of Eq. 4-7)."""
+    w = _f64(w)
+    return w - lr * (coef * _f64(u) + weight_decay * w)
+
+
 def is_refresh_step(step: int, period_k: int) -> bool:
     """Reading R4: NS5 refresh iff step % K == 0 ([ABS]: once every K steps)."""
     if period_k < 1:
@@ -139,31 +189,41 @@ def rownorm_update_direction(m, hp: OracleHParams) -> np.ndarray:
     return hp.gamma * row_normalise(m, hp.eps)
 
 
+def _step(w, m_prev, grad, refresh: bool, hp: OracleHParams):
+    m = momentum(m_prev, grad, hp.mu)
+    if refresh:
+        u, kind = ns5_update_direction(m, hp), "ns5"
+    else:
+        u, kind = rownorm_update_direction(m, hp), "rownorm"
+    coef = direction_scale(u, m.shape, kind, hp)
+    w_new = apply_update(w, u, coef, hp.lr, hp.weight_decay)
+    return w_new, m, coef * rms(u)
+
+
 def muon_step(w, m_prev, grad, step: int, hp: OracleHParams = OracleHParams()):
     """One Periodic Row-wise Muon step for one [A, B] matrix; returns (W_t, M_t).
 
     Momentum every step (Eq. 1, R5); on refresh steps (R4) the direction is
-    NS5(M_t), otherwise gamma * RowNorm(M_t) (R1, R2); the update is Eq. 4 with
-    weight decay on both kinds of step (R6, R7). period_k = 1 is vanilla Muon.
+    NS5(M_t), otherwise gamma * RowNorm(M_t) (R1, R2); the update is Eq. 4 (or the
+    scale rule hp.scale_mode selects, R14, R15) with weight decay on both kinds of
+    step (R6, R7). period_k = 1 is vanilla Muon.
     """
-    m = momentum(m_prev, grad, hp.mu)
-    if is_refresh_step(step, hp.period_k):
-        u = ns5_update_direction(m, hp)
-    else:
-        u = rownorm_update_direction(m, hp)
-    w_new = scaled_update(w, u, hp.lr, hp.weight_decay, hp.rms_scale)
+    w_new, m, _ = _step(w, m_prev, grad, is_refresh_step(step, hp.period_k), hp)
     return w_new, m
+
+
+def muon_step_monitored(w, m_prev, grad, step: int, hp: OracleHParams = OracleHParams()):
+    """muon_step plus the step's update RMS (R16); returns (W_t, M_t, rms)."""
+    return _step(w, m_prev, grad, is_refresh_step(step, hp.period_k), hp)
 
 
 def rownorm_step(w, m_prev, grad, hp: OracleHParams = OracleHParams()):
     """A non-refresh step regardless of the schedule; returns (W_t, M_t)."""
-    m = momentum(m_prev, grad, hp.mu)
-    u = rownorm_update_direction(m, hp)
-    return scaled_update(w, u, hp.lr, hp.weight_decay, hp.rms_scale), m
+    w_new, m, _ = _step(w, m_prev, grad, False, hp)
+    return w_new, m
 
 
 def vanilla_step(w, m_prev, grad, hp: OracleHParams = OracleHParams()):
     """A refresh (vanilla Muon) step regardless of the schedule; returns (W_t, M_t)."""
-    m = momentum(m_prev, grad, hp.mu)
-    u = ns5_update_direction(m, hp)
-    return scaled_update(w, u, hp.lr, hp.weight_decay, hp.rms_scale), m
+    w_new, m, _ = _step(w, m_prev, grad, True, hp)
+    return w_new, m
