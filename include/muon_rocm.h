@@ -37,22 +37,38 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 1
+#define MUON_ABI_VERSION 2
 
 /* Status codes returned by every entry point. */
 #define MUON_OK 0
 #define MUON_ERR_INVALID_ARG (-1) /* NULL where a pointer is required, negative dims,
-                                     count < 0, ns_steps < 1, period_k < 1, eps <= 0 */
+                                     count < 0, ns_steps < 1, period_k < 1, eps <= 0,
+                                     unknown scale_mode, hidden < 1 under MUON_SCALE_HIDDEN */
 #define MUON_ERR_WORKSPACE (-2)   /* workspace NULL or smaller than required */
-#define MUON_ERR_ALIGN (-3)       /* matrix pointer not 16-byte aligned, workspace not 256 */
+#define MUON_ERR_ALIGN (-3)       /* matrix pointer not 16-byte aligned, workspace not 256,
+                                     update_rms not 4 */
 #define MUON_ERR_ALIAS (-4)       /* overlapping buffers that must be distinct */
 #define MUON_ERR_HIP (-5)         /* a HIP runtime call or kernel launch failed */
 #define MUON_ERR_TOO_LARGE (-6)   /* a dimension above 2^30 or a matrix above 2^40 elements */
 
+/* Update-scale rules ("Muon is Scalable for LLM Training", Sec. 3.1). The update is
+ * W <- W - lr (c U + wd W) with U = O on refresh steps and U = gamma R on RowNorm
+ * steps, and the factor c is
+ *   MUON_SCALE_MAX_DIM: rms_scale sqrt(max(A,B))     (Eq. 4, the same as Eq. 7)
+ *   MUON_SCALE_HIDDEN:  rms_scale sqrt(hidden)        (Eq. 5, H = the model's hidden size)
+ *   MUON_SCALE_RMS:     rms_scale / max(RMS(O), eps)  (Eq. 6) on refresh steps, where
+ *                       RMS(O) = sqrt(mean(O^2)) is measured on the device; on RowNorm
+ *                       steps rms_scale sqrt(max(A,B)), since RMS(R) = 1/sqrt(max(A,B))
+ *                       exactly when every row (column) norm is >= eps. */
+#define MUON_SCALE_MAX_DIM 0
+#define MUON_SCALE_HIDDEN 1
+#define MUON_SCALE_RMS 2
+
 /* Hyperparameters. muon_default_hparams() fills the pages' defaults:
  * lr 1e-3, weight_decay 0.1, mu 0.95 (Muon notes Sec. 2.2), a, b, c =
  * 3.4445, -4.7750, 2.0315 (Sec. 2.1), rms_scale 0.2 (Eq. 4), gamma 0.15 and
- * period_k 3 (DiT paper, K/gamma sweep), eps 1e-7, ns_steps 5 (Sec. 2.2). */
+ * period_k 3 (DiT paper, K/gamma sweep), eps 1e-7, ns_steps 5 (Sec. 2.2),
+ * scale_mode MUON_SCALE_MAX_DIM, hidden 0. */
 typedef struct muon_hparams {
     float lr;           /* eta */
     float weight_decay; /* lambda, decoupled (Eq. 3/4) */
@@ -63,6 +79,8 @@ typedef struct muon_hparams {
     float eps;          /* norms are divided as x / max(norm, eps) */
     int32_t ns_steps;   /* N, Newton-Schulz iterations (>= 1) */
     int32_t period_k;   /* K, refresh period (>= 1; 1 = vanilla Muon) */
+    int32_t scale_mode; /* MUON_SCALE_* above */
+    int32_t hidden;     /* H of MUON_SCALE_HIDDEN (>= 1 there, ignored otherwise) */
 } muon_hparams;
 
 /* One weight matrix with its optimizer state. All three are [rows, cols]. */
@@ -84,7 +102,9 @@ typedef struct muon_matrix {
 #define MUON_KCLASS_COLNORM_PARTIAL 7  /* tall: momentum + per-column partial sums */
 #define MUON_KCLASS_COLNORM_FINALIZE 8 /* tall: per-column 1 / max(norm, eps) */
 #define MUON_KCLASS_COLNORM_APPLY 9    /* tall: Eq. 4 update with the column-normalised M */
-#define MUON_KCLASS_COUNT 10
+#define MUON_KCLASS_RMS_FINALIZE 10    /* per-matrix RMS(U): monitor value, Eq. 6 factor */
+#define MUON_KCLASS_SCALED_UPDATE 11   /* Eq. 6 refresh: W <- decay W - coef O */
+#define MUON_KCLASS_COUNT 12
 
 /* Returns MUON_ABI_VERSION. Host only. */
 int muon_abi_version(void);
@@ -107,12 +127,20 @@ int muon_workspace_bytes(const int64_t* rows, const int64_t* cols, int32_t count
 /* One optimizer step at 0-based step index `step` for `count` matrices.
  * Periodic schedule (DiT paper, "NS5 once every K steps"; read here as a refresh
  * iff step % period_k == 0, so step 0 refreshes and period_k == 1 is vanilla Muon):
- *   refresh:  M <- mu M + G;  O = NS5(M);  W <- W - lr (rms_scale sqrt(max(A,B)) O + wd W)
+ *   refresh:  M <- mu M + G;  O = NS5(M);  W <- W - lr (c O + wd W), c per scale_mode
+ *             (Eq. 4 and Eq. 5 fuse the update into the last Newton-Schulz GEMM;
+ *             Eq. 6 writes O to the workspace, reduces RMS(O), then updates W)
  *   otherwise: exactly rownorm_update() below.
- * mats: host array of `count` descriptors. Errors: INVALID_ARG, ALIGN, ALIAS (any two
- * of all w, m, g ranges overlap), WORKSPACE, TOO_LARGE, HIP. */
+ * mats: host array of `count` descriptors.
+ * update_rms: optional DEVICE array of `count` floats (NULL = not wanted). Entry i
+ *   receives RMS(c U_i), the RMS of the update direction before the learning rate,
+ *   weight decay excluded (about rms_scale under Eq. 4 by Lemma 1, exactly rms_scale
+ *   under Eq. 6); entries of skipped empty matrices are left unchanged. It must not
+ *   overlap any other buffer.
+ * Errors: INVALID_ARG, ALIGN, ALIAS (any two of all w, m, g, update_rms ranges
+ * overlap), WORKSPACE, TOO_LARGE, HIP. */
 int muon_step(const muon_matrix* mats, int32_t count, const muon_hparams* hp, int64_t step,
-              void* workspace, size_t workspace_bytes, void* stream);
+              void* workspace, size_t workspace_bytes, float* update_rms, void* stream);
 
 /* Newton-Schulz orthogonalisation alone ("Muon is Scalable", Sec. 2.1 Eq. 2):
  * o_out[i] = NS_N(m_in[i]) with X0 = M / max(||M||_F, eps), for [rows[i], cols[i]]
@@ -131,10 +159,11 @@ int ns5_batched(const float* const* m_in, float* const* o_out, const int64_t* ro
  *   M <- mu M + G
  *   R = M / max(row l2 norms, eps)     if rows <= cols
  *   R = M / max(column l2 norms, eps)  if rows >  cols
- *   W <- W - lr (rms_scale gamma sqrt(max(A,B)) R + wd W)
- * Errors as muon_step. */
+ *   W <- W - lr (c gamma R + wd W), c = rms_scale sqrt(max(A,B)) or rms_scale sqrt(hidden)
+ * update_rms as for muon_step (here RMS(c gamma R), one more small kernel when given).
+ * hp->period_k is not used. Errors as muon_step. */
 int rownorm_update(const muon_matrix* mats, int32_t count, const muon_hparams* hp,
-                   void* workspace, size_t workspace_bytes, void* stream);
+                   void* workspace, size_t workspace_bytes, float* update_rms, void* stream);
 
 /* Optional per-kernel-class timing. While enabled (enable != 0), every kernel the
  * library enqueues is bracketed by HIP events recorded on the caller's stream.

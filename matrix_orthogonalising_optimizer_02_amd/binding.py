@@ -20,8 +20,14 @@ MUON_ERR_ALIAS = -4
 MUON_ERR_HIP = -5
 MUON_ERR_TOO_LARGE = -6
 
+# update-scale rules (include/muon_rocm.h)
+SCALE_MAX_DIM = 0   # 0.2 sqrt(max(A, B)), Eq. 4 / Eq. 7
+SCALE_HIDDEN = 1    # 0.2 sqrt(H), Eq. 5
+SCALE_RMS = 2       # 0.2 / RMS(O), Eq. 6
+
 KCLASS_NAMES = ("cast", "frob", "gram", "poly", "apply", "apply_final", "rownorm_rows",
-                "colnorm_partial", "colnorm_finalize", "colnorm_apply")
+                "colnorm_partial", "colnorm_finalize", "colnorm_apply", "rms_finalize",
+                "scaled_update")
 
 EXPORTED = ("muon_abi_version", "muon_status_str", "muon_last_error", "muon_default_hparams",
             "muon_workspace_bytes", "muon_step", "ns5_batched", "rownorm_update",
@@ -34,6 +40,7 @@ class MuonHParams(ctypes.Structure):
         ("ns_a", ctypes.c_float), ("ns_b", ctypes.c_float), ("ns_c", ctypes.c_float),
         ("rms_scale", ctypes.c_float), ("gamma", ctypes.c_float), ("eps", ctypes.c_float),
         ("ns_steps", ctypes.c_int32), ("period_k", ctypes.c_int32),
+        ("scale_mode", ctypes.c_int32), ("hidden", ctypes.c_int32),
     ]
 
 
@@ -72,10 +79,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.muon_default_hparams.restype = None
     lib.muon_workspace_bytes.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64), i32,
                                          ctypes.POINTER(ctypes.c_size_t)]
-    lib.muon_step.argtypes = [ctypes.POINTER(MuonMatrix), i32, ctypes.POINTER(MuonHParams), i64, vp, sz, vp]
+    lib.muon_step.argtypes = [ctypes.POINTER(MuonMatrix), i32, ctypes.POINTER(MuonHParams), i64, vp, sz, vp, vp]
     lib.ns5_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_int64),
                                 ctypes.POINTER(ctypes.c_int64), i32, ctypes.POINTER(MuonHParams), vp, sz, vp]
-    lib.rownorm_update.argtypes = [ctypes.POINTER(MuonMatrix), i32, ctypes.POINTER(MuonHParams), vp, sz, vp]
+    lib.rownorm_update.argtypes = [ctypes.POINTER(MuonMatrix), i32, ctypes.POINTER(MuonHParams), vp, sz, vp, vp]
     lib.muon_timing_enable.argtypes = [ctypes.c_int]
     lib.muon_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     for name in ("muon_step", "ns5_batched", "rownorm_update", "muon_workspace_bytes",
@@ -165,27 +172,44 @@ def _matrices(weights, momenta, grads):
     return arr
 
 
+def _monitor_ptr(update_rms, count):
+    """Device pointer of an optional float32 [count] tensor for the update-RMS monitor."""
+    if update_rms is None:
+        return ctypes.c_void_p(None)
+    torch = _torch()
+    if not isinstance(update_rms, torch.Tensor) or update_rms.dtype != torch.float32 \
+            or update_rms.dim() != 1 or not update_rms.is_contiguous() or update_rms.numel() != count:
+        raise ValueError("update_rms must be a contiguous float32 tensor with one entry per matrix")
+    if count and update_rms.device.type != "cuda":
+        raise ValueError("update_rms must live on a GPU")
+    return ctypes.c_void_p(update_rms.data_ptr() or None)
+
+
 def muon_step(weights, momenta, grads, step: int, hp: Optional[MuonHParams] = None,
-              workspace=None, stream=None):
-    """One Periodic Row-wise Muon step (refresh iff step % period_k == 0), in place."""
+              workspace=None, stream=None, update_rms=None):
+    """One Periodic Row-wise Muon step (refresh iff step % period_k == 0), in place.
+
+    update_rms: optional float32 device tensor [len(weights)] that receives each
+    matrix's update RMS (RMS of the scaled direction, before lr and weight decay).
+    """
     hp = hp or default_hparams()
     arr = _matrices(weights, momenta, grads)
     dev = weights[0].device if weights else None
     ws, wsb = _ws(workspace, [tuple(w.shape) for w in weights], dev)
     rc = load_library().muon_step(arr, len(weights), ctypes.byref(hp), int(step), ws, wsb,
-                                  _stream_handle(stream, dev))
+                                  _monitor_ptr(update_rms, len(weights)), _stream_handle(stream, dev))
     _check(rc, "muon_step")
 
 
 def rownorm_update(weights, momenta, grads, hp: Optional[MuonHParams] = None, workspace=None,
-                   stream=None):
-    """The Periodic variant's RowNorm step, in place."""
+                   stream=None, update_rms=None):
+    """The Periodic variant's RowNorm step, in place (update_rms as for muon_step)."""
     hp = hp or default_hparams()
     arr = _matrices(weights, momenta, grads)
     dev = weights[0].device if weights else None
     ws, wsb = _ws(workspace, [tuple(w.shape) for w in weights], dev)
     rc = load_library().rownorm_update(arr, len(weights), ctypes.byref(hp), ws, wsb,
-                                       _stream_handle(stream, dev))
+                                       _monitor_ptr(update_rms, len(weights)), _stream_handle(stream, dev))
     _check(rc, "rownorm_update")
 
 
@@ -246,9 +270,9 @@ class MuonOptimizer:
                                         self.params[0].device if self.params else "cuda")
         self.step_count = 0
 
-    def step(self, grads, stream=None):
+    def step(self, grads, stream=None, update_rms=None):
         muon_step(self.params, self.momenta, list(grads), self.step_count, self.hp,
-                  self.workspace, stream)
+                  self.workspace, stream, update_rms)
         self.step_count += 1
 
     def state_dict(self):

@@ -417,6 +417,7 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         ld_t = d.m_p;
     }
     const float g2 = first_s * first_s;
+    float sq = 0.f;  // final modes: this lane's sum of O^2 (padding contributes exact zeros)
 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -458,6 +459,7 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
                             else x = fmaf(args.ca, o, x) * first_s;
                         }
                         v[e] = x;
+                        if constexpr (!kBf16Out) sq = fmaf(x, x, sq);
                     }
                     if constexpr (kBf16Out) {
                         unsigned short hv[4];
@@ -570,6 +572,13 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         }
         // the next half overwrites the staging area: LDS executes a wave's operations in
         // order, so its writes cannot overtake the reads above
+    }
+    if constexpr (!kBf16Out) {
+        static_assert(NT == 256, "four per-wave partials per tile");
+        if (d.part) {
+            const float t = wave_sum(sq);
+            if (lane == 0) d.part[local * 4 + wave] = t;
+        }
     }
 }
 

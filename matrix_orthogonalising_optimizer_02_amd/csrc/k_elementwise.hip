@@ -191,7 +191,9 @@ __global__ __launch_bounds__(256) void k_rownorm_rows(RowArgs args) {
             }
         }
         const float tot = block_sum_256(ss, red);
-        const float c = d.coef / max_keep_nan(sqrtf(tot), args.eps);
+        const float den = max_keep_nan(sqrtf(tot), args.eps);
+        const float c = d.coef / den;
+        if (d.part && tid == 0) d.part[row] = tot / (den * den);
         const float decay = args.decay;
 #pragma unroll
         for (int k0 = 0; k0 < VMAX; k0 += kB) {
@@ -225,7 +227,9 @@ __global__ __launch_bounds__(256) void k_rownorm_rows(RowArgs args) {
             }
         }
         const float tot = block_sum_256(ss, red);
-        const float c = d.coef / max_keep_nan(sqrtf(tot), args.eps);
+        const float den = max_keep_nan(sqrtf(tot), args.eps);
+        const float c = d.coef / den;
+        if (d.part && tid == 0) d.part[row] = tot / (den * den);
         const float decay = args.decay;
 #pragma unroll
         for (int k = 0; k < VMAX * 4; ++k) {
@@ -252,7 +256,9 @@ __global__ __launch_bounds__(256) void k_rownorm_rows_long(RowArgs args) {
     }
     // each thread re-reads only the elements it wrote itself, so no fence is needed
     const float tot = block_sum_256(ss, red);
-    const float c = d.coef / max_keep_nan(sqrtf(tot), args.eps);
+    const float den = max_keep_nan(sqrtf(tot), args.eps);
+    const float c = d.coef / den;
+    if (d.part && threadIdx.x == 0) d.part[row] = tot / (den * den);
     for (int idx = threadIdx.x; idx < d.cols; idx += 256)
         d.w[base + idx] = fmaf(-c, d.m[base + idx], d.w[base + idx] * args.decay);
 }
@@ -360,7 +366,9 @@ __global__ __launch_bounds__(256) void k_colnorm_finalize(ColArgs args) {
     if (c >= d.cols) return;
     float s = 0.f;
     for (int k = 0; k < d.chunks; ++k) s += d.partial[(int64_t)k * d.cols + c];
-    d.inv[c] = 1.0f / max_keep_nan(sqrtf(s), args.eps);
+    const float den = max_keep_nan(sqrtf(s), args.eps);
+    d.inv[c] = 1.0f / den;
+    if (d.part) d.part[c] = s / (den * den);
 }
 
 template <bool VEC>
@@ -432,6 +440,74 @@ hipError_t launch_colnorm_finalize(const ColArgs& a, int fin_total, hipStream_t 
 hipError_t launch_colnorm_apply(const ColArgs& a, bool vec, hipStream_t s) {
     if (vec) hipLaunchKernelGGL(k_colnorm_apply<true>, dim3(a.total), dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_colnorm_apply<false>, dim3(a.total), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------- update RMS ----
+// One block per matrix: RMS(U) from the partial sums of U^2 (fixed order, double),
+// then the monitor value and, for the Eq. 6 rule ("Muon is Scalable for LLM
+// Training", Sec. 3.1 Eq. 6), the per-matrix update coefficient lr * 0.2 / RMS(O).
+__global__ __launch_bounds__(256) void k_rms_finalize(RmsArgs args) {
+    __shared__ double red[4];
+    const RmsDesc& d = args.d[blockIdx.x];
+    double acc = 0.0;
+    for (int i = threadIdx.x; i < d.count; i += 256) acc += (double)d.part[i];
+    acc = wave_sum_d(acc);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const double tot = (red[0] + red[1]) + (red[2] + red[3]);
+        const double r = sqrt(tot / d.elems);
+        double mon;
+        if (d.eq6) {
+            const double den = r < (double)args.eps ? (double)args.eps : r;  // NaN stays NaN
+            *d.coef_out = (float)((double)args.lr * (double)args.rms_scale / den);
+            mon = (double)args.rms_scale * r / den;
+        } else {
+            mon = (double)d.dir_scale * r;
+        }
+        if (d.rms_out) *d.rms_out = (float)mon;
+    }
+}
+
+hipError_t launch_rms_finalize(const RmsArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(k_rms_finalize, dim3(a.n), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// W <- decay W - coef O, the Eq. 6 update once RMS(O) is known. 16 elements per
+// thread as four float4, loads of a block issued before its stores.
+__global__ __launch_bounds__(256) void k_scaled_update(UpdArgs args) {
+    const int t = blockIdx.x;
+    int gi = 0;
+    while (gi + 1 < args.n && t >= args.d[gi + 1].blk_begin) ++gi;
+    const UpdDesc& d = args.d[gi];
+    const float coef = *d.coef, decay = args.decay;
+    const int64_t base = (int64_t)(t - d.blk_begin) * kUpdBlockElems;
+    constexpr int kV = kUpdBlockElems / 256 / 4;
+    if (base + kUpdBlockElems <= d.elems) {
+        floatx4 ov[kV], wv[kV];
+#pragma unroll
+        for (int k = 0; k < kV; ++k) {
+            const int64_t i = base + (int64_t)(k * 256 + threadIdx.x) * 4;
+            ov[k] = *reinterpret_cast<const floatx4*>(d.o + i);
+            wv[k] = *reinterpret_cast<const floatx4*>(d.w + i);
+        }
+#pragma unroll
+        for (int k = 0; k < kV; ++k) {
+            const int64_t i = base + (int64_t)(k * 256 + threadIdx.x) * 4;
+            floatx4 w = wv[k];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = fmaf(-coef, ov[k][e], w[e] * decay);
+            *reinterpret_cast<floatx4*>(d.w + i) = w;
+        }
+    } else {
+        for (int64_t i = base + threadIdx.x; i < d.elems; i += 256) d.w[i] = fmaf(-coef, d.o[i], d.w[i] * decay);
+    }
+}
+
+hipError_t launch_scaled_update(const UpdArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(k_scaled_update, dim3(a.total), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -66,7 +66,8 @@ struct NsDesc {
     int32_t tall;
     int32_t ntiles;        // tiles of this matrix in the stage
     int32_t tiles;         // symmetric: tiles per side; rectangular: tiles along n
-    float upd_coef;        // lr * rms_scale * sqrt(n)
+    float upd_coef;        // lr * (the update's direction scale), fused Eq. 4 / 5 update
+    float* part;           // final modes, optional: [ntiles * 4] per-wave sums of O^2
 };
 
 struct NsArgs {
@@ -85,7 +86,8 @@ struct RowDesc {
     float* w;
     int32_t rows, cols;
     int32_t row_begin;     // first block of this matrix in the launch
-    float coef;            // lr * rms_scale * gamma * sqrt(max(rows, cols))
+    float coef;            // lr * gamma * (the update's direction scale)
+    float* part;           // optional: [rows] sums of R^2 per row
 };
 
 struct RowArgs {
@@ -107,6 +109,7 @@ struct ColDesc {
     int32_t tile_begin;    // first block of this matrix in the launch
     int32_t fin_begin;     // first block of this matrix in the finalize launch
     float coef;
+    float* part;           // optional: [cols] sums of R^2 per column
 };
 
 struct ColArgs {
@@ -115,6 +118,46 @@ struct ColArgs {
     int32_t total;
     float mu, decay, eps;
 };
+
+// ---- update RMS and the Eq. 6 scale -------------------------------------------
+// One block per matrix sums `count` partial sums of U^2 (fixed order, double) into
+// RMS(U) = sqrt(sum / elems). Eq. 6 refresh (eq6 != 0): coef_out = lr * rms_scale /
+// max(RMS(O), eps) and the monitor reads rms_scale * RMS(O) / max(RMS(O), eps).
+// Otherwise the monitor reads dir_scale * RMS(U).
+struct RmsDesc {
+    const float* part;
+    float* coef_out;       // eq6: device scalar for the update kernel
+    float* rms_out;        // optional: the caller's monitor entry
+    double elems;          // rows * cols
+    float dir_scale;
+    int32_t count;
+    int32_t eq6;
+};
+
+struct RmsArgs {
+    RmsDesc d[kMaxGroup];
+    int32_t n;
+    float lr, rms_scale, eps;
+};
+
+// W <- decay W - coef O over [rows, cols] (O fp32, same layout as W); 4096 elements
+// per block.
+struct UpdDesc {
+    const float* o;
+    float* w;
+    const float* coef;     // device scalar
+    int64_t elems;
+    int32_t blk_begin;
+};
+
+struct UpdArgs {
+    UpdDesc d[kMaxGroup];
+    int32_t n;
+    int32_t total;
+    float decay;
+};
+
+constexpr int kUpdBlockElems = 4096;
 
 constexpr int kColChunkRows = 256;
 constexpr int kColTileCols = 256;
@@ -130,6 +173,8 @@ hipError_t launch_rownorm_rows(const RowArgs& a, int max_cols, bool vec, hipStre
 hipError_t launch_colnorm_partial(const ColArgs& a, bool vec, hipStream_t s);
 hipError_t launch_colnorm_finalize(const ColArgs& a, int fin_total, hipStream_t s);
 hipError_t launch_colnorm_apply(const ColArgs& a, bool vec, hipStream_t s);
+hipError_t launch_rms_finalize(const RmsArgs& a, hipStream_t s);
+hipError_t launch_scaled_update(const UpdArgs& a, hipStream_t s);
 
 // GEMM block tiles (host-side tile counting must match the kernels).
 #ifndef MUON_GEMM_BIG_M

@@ -5,8 +5,12 @@
 // Row-wise paragraphs):
 //   refresh step:  cast (M <- mu M + G, ||M||^2 partials, bf16 X_r / X_c)
 //                  -> frob (s = 1 / max(||M||_F, eps))
-//                  -> N x [gram, poly, apply]; the last apply applies Eq. 4 to W
+//                  -> N x [gram, poly, apply]; the last apply applies Eq. 4 (Eq. 5) to W,
+//                     or, under Eq. 6 (Sec. 3.1), writes fp32 O over the two X_r buffers
+//                     (free by then) -> RMS(O) -> W <- decay W - lr 0.2 / RMS(O) O
 //   RowNorm step:  rows kernel (flat / square) or partial -> finalize -> apply (tall)
+//   update-RMS monitor (optional): the last apply / the RowNorm kernels leave partial
+//                  sums of U^2 in the workspace; one finalize kernel per group reduces them
 // Matrices are planned in groups of up to kMaxGroup, ordered by working size m and
 // then by n (largest first), and each group's kernels cover all of its matrices in
 // one launch per stage. Groups run one after another on the caller's stream and
@@ -52,9 +56,12 @@ struct MatPlan {
     int64_t m, n, m_p, n_p;   // working dims and padded dims
     int64_t rows_p, cols_p;   // padded dims in the input orientation
     int64_t cast_tiles;
+    int64_t max_tiles;        // final-apply tiles with the smallest tile (partial sums)
     // workspace offsets (relative to the group base)
-    size_t xr[2], xc[2], a, b, partial, scale;  // refresh
+    size_t xr[2], xc[2], a, b, partial, scale;  // refresh; xr[0], xr[1] are adjacent
+    size_t rpart, coef;                         // refresh: per-wave O^2 sums, Eq. 6 factor
     size_t colpart, inv;                        // RowNorm, tall only
+    size_t rpart_rn;                            // RowNorm: per-line R^2 sums
     int64_t chunks;
 };
 
@@ -88,6 +95,7 @@ int make_plan(const int64_t* rows, const int64_t* cols, int32_t count, Plan* pla
         p.rows_p = p.tall ? p.n_p : p.m_p;
         p.cols_p = p.tall ? p.m_p : p.n_p;
         p.cast_tiles = (p.rows_p / 64) * (p.cols_p / 64);
+        p.max_tiles = (p.m_p / kGemmSmall) * (p.n_p / kGemmSmall);
         p.chunks = (r + kColChunkRows - 1) / kColChunkRows;
         all.push_back(p);
     }
@@ -100,17 +108,22 @@ int make_plan(const int64_t* rows, const int64_t* cols, int32_t count, Plan* pla
     for (size_t s = 0; s < all.size(); s += kMaxGroup) {
         GroupPlan gp;
         size_t ns = 0, rn = 0;
-        int64_t cast_total = 0, rows_total = 0, col_total = 0;
+        int64_t cast_total = 0, rows_total = 0, col_total = 0, upd_total = 0;
         for (size_t k = s; k < std::min(all.size(), s + kMaxGroup); ++k) {
             MatPlan p = all[k];
             const size_t xbytes = size_t(p.m_p) * size_t(p.n_p) * 2;
             const size_t abytes = size_t(p.m_p) * size_t(p.m_p) * 2;
+            // xbytes is a multiple of 256: xr[1] starts where xr[0] ends, so together they
+            // hold an fp32 [rows, cols] O for the Eq. 6 update
             for (int q = 0; q < 2; ++q) { p.xr[q] = ns; ns = align256(ns + xbytes); }
             for (int q = 0; q < 2; ++q) { p.xc[q] = ns; ns = align256(ns + xbytes); }
             p.a = ns; ns = align256(ns + abytes);
             p.b = ns; ns = align256(ns + abytes);
             p.partial = ns; ns = align256(ns + size_t(p.cast_tiles) * 4);
             p.scale = ns; ns = align256(ns + 4);
+            p.rpart = ns; ns = align256(ns + size_t(p.max_tiles) * 4 * 4);
+            p.coef = ns; ns = align256(ns + 4);
+            p.rpart_rn = rn; rn = align256(rn + size_t(p.tall ? p.cols : p.rows) * 4);
             if (p.tall) {
                 p.colpart = rn; rn = align256(rn + size_t(p.chunks) * size_t(p.cols) * 4);
                 p.inv = rn; rn = align256(rn + size_t(p.cols) * 4);
@@ -119,10 +132,12 @@ int make_plan(const int64_t* rows, const int64_t* cols, int32_t count, Plan* pla
                 rows_total += p.rows;
             }
             cast_total += p.cast_tiles;
+            upd_total += (p.rows * p.cols + kUpdBlockElems - 1) / kUpdBlockElems;
             gp.mats.push_back(p);
         }
         const int64_t tile_total_cap = int64_t(1) << 31;
-        if (cast_total >= tile_total_cap || rows_total >= tile_total_cap || col_total >= tile_total_cap)
+        if (cast_total >= tile_total_cap || rows_total >= tile_total_cap || col_total >= tile_total_cap ||
+            upd_total >= tile_total_cap)
             return fail(MUON_ERR_TOO_LARGE, "a launch would exceed 2^31 workgroups");
         gp.bytes = std::max(ns, rn);
         plan->bytes = std::max(plan->bytes, gp.bytes);
@@ -184,7 +199,19 @@ int check_hparams(const muon_hparams* hp, bool need_steps) {
     if (hp->ns_steps < 1 || hp->ns_steps > kMaxNsSteps)
         return fail(MUON_ERR_INVALID_ARG, "ns_steps must be in [1, 100]");
     if (need_steps && hp->period_k < 1) return fail(MUON_ERR_INVALID_ARG, "period_k must be >= 1");
+    if (hp->scale_mode != MUON_SCALE_MAX_DIM && hp->scale_mode != MUON_SCALE_HIDDEN &&
+        hp->scale_mode != MUON_SCALE_RMS)
+        return fail(MUON_ERR_INVALID_ARG, "unknown scale_mode");
+    if (hp->scale_mode == MUON_SCALE_HIDDEN && hp->hidden < 1)
+        return fail(MUON_ERR_INVALID_ARG, "hidden must be >= 1 under MUON_SCALE_HIDDEN");
     return MUON_OK;
+}
+
+// The factor of the update direction before the learning rate (Eq. 4 / Eq. 5; the
+// Eq. 6 refresh factor is computed on the device).
+double dir_scale(const muon_hparams& hp, int64_t n) {
+    const double h = hp.scale_mode == MUON_SCALE_HIDDEN ? double(hp.hidden) : double(n);
+    return double(hp.rms_scale) * std::sqrt(h);
 }
 
 struct Range {
@@ -201,6 +228,14 @@ int check_overlaps(std::vector<Range>& rs) {
         hi_any = std::max(hi_any, r.hi);
         if (r.write) hi_write = std::max(hi_write, r.hi);
     }
+    return MUON_OK;
+}
+
+int check_monitor(const float* update_rms, int32_t count, std::vector<Range>& ranges) {
+    if (!update_rms || count == 0) return MUON_OK;
+    if (reinterpret_cast<uintptr_t>(update_rms) & 3) return fail(MUON_ERR_ALIGN, "update_rms not 4-byte aligned");
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(update_rms);
+    ranges.push_back({lo, lo + uintptr_t(count) * 4, true});
     return MUON_OK;
 }
 
@@ -296,8 +331,10 @@ GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym) {
 }
 
 int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_hparams& hp,
-                bool momentum, bool update_w, char* ws, hipStream_t s) {
+                bool momentum, bool update_w, char* ws, float* update_rms, hipStream_t s) {
     const int ng = int(gp.mats.size());
+    const bool eq6 = update_w && hp.scale_mode == MUON_SCALE_RMS;
+    const bool monitor = update_w && update_rms != nullptr;
     // cast
     CastArgs ca{};
     ca.n = ng;
@@ -347,6 +384,7 @@ int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_h
     na.decay = 1.0f - hp.lr * hp.weight_decay;
     for (int it = 0; it < hp.ns_steps; ++it) {
         const int cur = it & 1, nxt = cur ^ 1;
+        const bool last = it + 1 == hp.ns_steps;
         na.first = it == 0 ? 1 : 0;
         for (int k = 0; k < ng; ++k) {
             const MatPlan& p = gp.mats[k];
@@ -357,14 +395,15 @@ int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_h
             d.xc_next = reinterpret_cast<unsigned short*>(ws + p.xc[nxt]);
             d.a = reinterpret_cast<unsigned short*>(ws + p.a);
             d.b = reinterpret_cast<unsigned short*>(ws + p.b);
-            d.out = io[k].out;
+            d.out = (last && eq6) ? reinterpret_cast<float*>(ws + p.xr[0]) : io[k].out;
+            d.part = (last && (eq6 || monitor)) ? reinterpret_cast<float*>(ws + p.rpart) : nullptr;
             d.scale = reinterpret_cast<const float*>(ws + p.scale);
             d.m = int32_t(p.m);
             d.n = int32_t(p.n);
             d.m_p = int32_t(p.m_p);
             d.n_p = int32_t(p.n_p);
             d.tall = p.tall ? 1 : 0;
-            d.upd_coef = float(double(hp.lr) * double(hp.rms_scale) * std::sqrt(double(p.n)));
+            d.upd_coef = float(double(hp.lr) * dir_scale(hp, p.n));
         }
         const GemmTile sym_tile = plan_tiles(gp, na, true);
         rc = run_kernel(MUON_KCLASS_GRAM, s, "gram", [&] { return launch_ns_gemm(kModeGram, sym_tile, na, s); });
@@ -372,17 +411,55 @@ int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_h
         rc = run_kernel(MUON_KCLASS_POLY, s, "poly", [&] { return launch_ns_gemm(kModePoly, sym_tile, na, s); });
         if (rc) return rc;
         const GemmTile apply_tile = plan_tiles(gp, na, false);
-        const bool last = it + 1 == hp.ns_steps;
-        const GemmMode mode = !last ? kModeApply : (update_w ? kModeFinalW : kModeFinalO);
+        const GemmMode mode = !last ? kModeApply : ((update_w && !eq6) ? kModeFinalW : kModeFinalO);
         rc = run_kernel(last ? MUON_KCLASS_APPLY_FINAL : MUON_KCLASS_APPLY, s, "apply",
                         [&] { return launch_ns_gemm(mode, apply_tile, na, s); });
+        if (rc) return rc;
+    }
+    if (eq6 || monitor) {
+        RmsArgs ra{};
+        ra.n = ng;
+        ra.lr = hp.lr;
+        ra.rms_scale = hp.rms_scale;
+        ra.eps = hp.eps;
+        for (int k = 0; k < ng; ++k) {
+            const MatPlan& p = gp.mats[k];
+            RmsDesc& r = ra.d[k];
+            r.part = reinterpret_cast<const float*>(ws + p.rpart);
+            r.count = na.d[k].ntiles * 4;  // the final apply's tiles, four waves each
+            r.elems = double(p.rows) * double(p.cols);
+            r.dir_scale = float(dir_scale(hp, p.n));
+            r.eq6 = eq6 ? 1 : 0;
+            r.coef_out = eq6 ? reinterpret_cast<float*>(ws + p.coef) : nullptr;
+            r.rms_out = update_rms ? update_rms + p.idx : nullptr;
+        }
+        rc = run_kernel(MUON_KCLASS_RMS_FINALIZE, s, "rms_finalize", [&] { return launch_rms_finalize(ra, s); });
+        if (rc) return rc;
+    }
+    if (eq6) {
+        UpdArgs ua{};
+        ua.n = ng;
+        ua.decay = na.decay;
+        int64_t blocks = 0;
+        for (int k = 0; k < ng; ++k) {
+            const MatPlan& p = gp.mats[k];
+            UpdDesc& u = ua.d[k];
+            u.o = reinterpret_cast<const float*>(ws + p.xr[0]);
+            u.w = io[k].out;
+            u.coef = reinterpret_cast<const float*>(ws + p.coef);
+            u.elems = p.rows * p.cols;
+            u.blk_begin = int32_t(blocks);
+            blocks += (u.elems + kUpdBlockElems - 1) / kUpdBlockElems;
+        }
+        ua.total = int32_t(blocks);
+        rc = run_kernel(MUON_KCLASS_SCALED_UPDATE, s, "scaled_update", [&] { return launch_scaled_update(ua, s); });
         if (rc) return rc;
     }
     return MUON_OK;
 }
 
 int run_rownorm(const GroupPlan& gp, const muon_matrix* mats, const muon_hparams& hp, char* ws,
-                hipStream_t s) {
+                float* update_rms, hipStream_t s) {
     const float decay = 1.0f - hp.lr * hp.weight_decay;
     RowArgs ra{};
     ra.mu = hp.mu;
@@ -397,7 +474,8 @@ int run_rownorm(const GroupPlan& gp, const muon_matrix* mats, const muon_hparams
     bool row_vec = true, col_vec = true;
     for (const MatPlan& p : gp.mats) {
         const muon_matrix& t = mats[p.idx];
-        const float coef = float(double(hp.lr) * double(hp.rms_scale) * double(hp.gamma) * std::sqrt(double(p.n)));
+        const float coef = float(double(hp.lr) * double(hp.gamma) * dir_scale(hp, p.n));
+        float* part = update_rms ? reinterpret_cast<float*>(ws + p.rpart_rn) : nullptr;
         if (!p.tall) {
             RowDesc& d = ra.d[ra.n++];
             d.g = t.g;
@@ -407,6 +485,7 @@ int run_rownorm(const GroupPlan& gp, const muon_matrix* mats, const muon_hparams
             d.cols = int32_t(p.cols);
             d.row_begin = int32_t(rows_total);
             d.coef = coef;
+            d.part = part;
             rows_total += p.rows;
             max_cols = std::max<int>(max_cols, int(p.cols));
             row_vec = row_vec && (p.cols % 4 == 0);
@@ -424,6 +503,7 @@ int run_rownorm(const GroupPlan& gp, const muon_matrix* mats, const muon_hparams
             d.tile_begin = int32_t(col_total);
             d.fin_begin = int32_t(fin_total);
             d.coef = coef;
+            d.part = part;
             col_total += int64_t(d.chunks) * d.tiles_c;
             fin_total += (p.cols + 255) / 256;
             col_vec = col_vec && (p.cols % 4 == 0);
@@ -446,18 +526,40 @@ int run_rownorm(const GroupPlan& gp, const muon_matrix* mats, const muon_hparams
         if (rc) return rc;
         rc = run_kernel(MUON_KCLASS_COLNORM_APPLY, s, "colnorm_apply",
                         [&] { return launch_colnorm_apply(ca, col_vec, s); });
+        if (rc) return rc;
+    }
+    if (update_rms) {
+        RmsArgs ra{};
+        ra.n = int32_t(gp.mats.size());
+        ra.lr = hp.lr;
+        ra.rms_scale = hp.rms_scale;
+        ra.eps = hp.eps;
+        for (int k = 0; k < ra.n; ++k) {
+            const MatPlan& p = gp.mats[k];
+            RmsDesc& r = ra.d[k];
+            r.part = reinterpret_cast<const float*>(ws + p.rpart_rn);
+            r.count = int32_t(p.tall ? p.cols : p.rows);
+            r.elems = double(p.rows) * double(p.cols);
+            r.dir_scale = float(double(hp.gamma) * dir_scale(hp, p.n));
+            r.eq6 = 0;
+            r.coef_out = nullptr;
+            r.rms_out = update_rms + p.idx;
+        }
+        rc = run_kernel(MUON_KCLASS_RMS_FINALIZE, s, "rms_finalize", [&] { return launch_rms_finalize(ra, s); });
     }
     return rc;
 }
 
 int do_rownorm(const muon_matrix* mats, int32_t count, const muon_hparams* hp, void* ws,
-               size_t ws_bytes, void* stream, bool need_k) {
+               size_t ws_bytes, float* update_rms, void* stream, bool need_k) {
     g_last_error.clear();
     int rc = check_hparams(hp, need_k);
     if (rc) return rc;
     std::vector<int64_t> rows, cols;
     std::vector<Range> ranges;
     rc = check_matrices(mats, count, rows, cols, ranges);
+    if (rc) return rc;
+    rc = check_monitor(update_rms, count, ranges);
     if (rc) return rc;
     Plan plan;
     rc = make_plan(rows.data(), cols.data(), count, &plan);
@@ -468,7 +570,7 @@ int do_rownorm(const muon_matrix* mats, int32_t count, const muon_hparams* hp, v
     if (rc) return rc;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     for (const GroupPlan& gp : plan.groups) {
-        rc = run_rownorm(gp, mats, *hp, static_cast<char*>(ws), s);
+        rc = run_rownorm(gp, mats, *hp, static_cast<char*>(ws), update_rms, s);
         if (rc) return rc;
     }
     return MUON_OK;
@@ -509,6 +611,8 @@ MUON_API void muon_default_hparams(muon_hparams* hp) {
     hp->eps = 1e-7f;
     hp->ns_steps = 5;
     hp->period_k = 3;
+    hp->scale_mode = MUON_SCALE_MAX_DIM;
+    hp->hidden = 0;
 }
 
 MUON_API int muon_workspace_bytes(const int64_t* rows, const int64_t* cols, int32_t count, size_t* bytes) {
@@ -524,16 +628,18 @@ MUON_API int muon_workspace_bytes(const int64_t* rows, const int64_t* cols, int3
 }
 
 MUON_API int muon_step(const muon_matrix* mats, int32_t count, const muon_hparams* hp, int64_t step,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       void* workspace, size_t workspace_bytes, float* update_rms, void* stream) {
     g_last_error.clear();
     if (step < 0) return fail(MUON_ERR_INVALID_ARG, "step < 0");
     int rc = check_hparams(hp, true);
     if (rc) return rc;
     if (step % hp->period_k != 0)
-        return do_rownorm(mats, count, hp, workspace, workspace_bytes, stream, true);
+        return do_rownorm(mats, count, hp, workspace, workspace_bytes, update_rms, stream, true);
     std::vector<int64_t> rows, cols;
     std::vector<Range> ranges;
     rc = check_matrices(mats, count, rows, cols, ranges);
+    if (rc) return rc;
+    rc = check_monitor(update_rms, count, ranges);
     if (rc) return rc;
     Plan plan;
     rc = make_plan(rows.data(), cols.data(), count, &plan);
@@ -549,7 +655,7 @@ MUON_API int muon_step(const muon_matrix* mats, int32_t count, const muon_hparam
             const muon_matrix& t = mats[p.idx];
             io.push_back({t.m, t.g, t.m, t.w});
         }
-        rc = run_refresh(gp, io, *hp, true, true, static_cast<char*>(workspace), s);
+        rc = run_refresh(gp, io, *hp, true, true, static_cast<char*>(workspace), update_rms, s);
         if (rc) return rc;
     }
     return MUON_OK;
@@ -593,15 +699,15 @@ MUON_API int ns5_batched(const float* const* m_in, float* const* o_out, const in
     for (const GroupPlan& gp : plan.groups) {
         std::vector<IoPtrs> io;
         for (const MatPlan& p : gp.mats) io.push_back({m_in[p.idx], nullptr, nullptr, o_out[p.idx]});
-        rc = run_refresh(gp, io, *hp, false, false, static_cast<char*>(workspace), s);
+        rc = run_refresh(gp, io, *hp, false, false, static_cast<char*>(workspace), nullptr, s);
         if (rc) return rc;
     }
     return MUON_OK;
 }
 
 MUON_API int rownorm_update(const muon_matrix* mats, int32_t count, const muon_hparams* hp,
-                            void* workspace, size_t workspace_bytes, void* stream) {
-    return do_rownorm(mats, count, hp, workspace, workspace_bytes, stream, false);
+                            void* workspace, size_t workspace_bytes, float* update_rms, void* stream) {
+    return do_rownorm(mats, count, hp, workspace, workspace_bytes, update_rms, stream, false);
 }
 
 MUON_API int muon_timing_enable(int enable) {

