@@ -74,6 +74,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2, help="untimed Periodic cycles")
     ap.add_argument("--workload", default="15b", choices=["15b", "mmdit3072", "bucket2048", "dit2048"])
     ap.add_argument("--vanilla-steps", type=int, default=4)
+    ap.add_argument("--variant-steps", type=int, default=2,
+                    help="timed steps per scale-rule / monitor variant (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
@@ -124,6 +126,52 @@ def cpu_baseline(wl, k):
                       f"{shape[0]}x{shape[1]} matrix, scaled by flops and elements to the {len(wl.shapes)}-matrix "
                       f"set; value = mean ms per optimizer step over a K={k} cycle",
             "vanilla_step_ms": round(1e3 * ref_total, 1), "rownorm_step_ms": round(1e3 * rn_total, 1)}
+
+
+def measure_variants(pkg, torch, weights, momenta, grads, ws, k, wl, n, say):
+    """Refresh steps under the Eq. 5 and Eq. 6 scale rules and a Periodic cycle with the
+    update-RMS monitor, on the same resident state (HIP events around each block)."""
+    shapes = [tuple(w.shape) for w in weights]
+    rms = torch.zeros(len(weights), dtype=torch.float32, device=weights[0].device)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    res = {}
+    hidden = max(max(s) for s in shapes if s[0] == s[1]) if any(s[0] == s[1] for s in shapes) else max(shapes[0])
+    hp5 = pkg.default_hparams(period_k=1, scale_mode=pkg.SCALE_HIDDEN, hidden=hidden)
+    res["eq5_refresh_step_ms"] = round(timed(lambda: pkg.muon_step(weights, momenta, grads[0], 0, hp5, ws)), 4)
+    res["eq5_hidden"] = hidden
+    hp6 = pkg.default_hparams(period_k=1, scale_mode=pkg.SCALE_RMS)
+    pkg.timing_enable(True)
+    res["eq6_refresh_step_ms"] = round(timed(lambda: pkg.muon_step(weights, momenta, grads[0], 0, hp6, ws)), 4)
+    kern = pkg.timing_read()
+    pkg.timing_enable(False)
+    for name, bytes_per_elem in (("rms_finalize", None), ("scaled_update", 12.0), ("apply_final", None)):
+        ms_, c = kern[name]
+        if c:
+            ent = {"avg_ms": round(ms_ / c, 4)}
+            if bytes_per_elem:
+                ent["algorithmic_gbs"] = round(bytes_per_elem * wl.elements / (ms_ / c * 1e-3) / 1e9, 1)
+            res[f"eq6_{name}"] = ent
+    hp = pkg.default_hparams(period_k=k)
+    hp1 = pkg.default_hparams(period_k=1)
+    res["monitored_refresh_step_ms"] = round(timed(
+        lambda: pkg.muon_step(weights, momenta, grads[0], 0, hp1, ws, update_rms=rms)), 4)
+    res["monitored_rownorm_step_ms"] = round(timed(
+        lambda: pkg.muon_step(weights, momenta, grads[1], 1, hp, ws, update_rms=rms)), 4)
+    res["unmonitored_rownorm_step_ms"] = round(timed(
+        lambda: pkg.muon_step(weights, momenta, grads[1], 1, hp, ws)), 4)
+    res["update_rms_last"] = [round(float(x), 5) for x in rms.cpu().tolist()]
+    say(f"variants: {res}")
+    return res
 
 
 def main():
@@ -204,6 +252,9 @@ def main():
     vanilla_ms = ev2.elapsed_time(ev3) / max(args.vanilla_steps, 1)
     say(f"vanilla: {vanilla_ms:.3f} ms per step")
 
+    variants = measure_variants(pkg, torch, weights, momenta, grads, ws, k, wl, args.variant_steps, say) \
+        if args.variant_steps > 0 else None
+
     refreshes = args.steps
     rownorm_steps = args.steps * (k - 1)
     ms = {name: kern[name][0] for name in kern}
@@ -273,6 +324,8 @@ def main():
                      "launch_ms": round(apply_launch_ms, 4), "launch_flops": apply_launch_flops},
         "kernels": kernels,
     }
+    if variants is not None:
+        out["variants"] = variants
     if not args.no_cpu_baseline:
         say("cpu baseline: timing the float64 oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(wl, k)

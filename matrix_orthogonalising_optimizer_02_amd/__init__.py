@@ -5,6 +5,9 @@ The work runs in libmuon_rocm.so (HIP kernels behind a C ABI, include/muon_rocm.
 inputs used by the tests and the benchmark.
 """
 from .binding import (  # noqa: F401
+    SCALE_HIDDEN,
+    SCALE_MAX_DIM,
+    SCALE_RMS,
     MuonError,
     MuonHParams,
     MuonOptimizer,
