@@ -104,7 +104,8 @@ typedef struct muon_matrix {
 #define MUON_KCLASS_COLNORM_APPLY 9    /* tall: Eq. 4 update with the column-normalised M */
 #define MUON_KCLASS_RMS_FINALIZE 10    /* per-matrix RMS(U): monitor value, Eq. 6 factor */
 #define MUON_KCLASS_SCALED_UPDATE 11   /* Eq. 6 refresh: W <- decay W - coef O */
-#define MUON_KCLASS_COUNT 12
+#define MUON_KCLASS_ADAMW 12           /* AdamW companion (non-matrix parameters) */
+#define MUON_KCLASS_COUNT 13
 
 /* Returns MUON_ABI_VERSION. Host only. */
 int muon_abi_version(void);
@@ -164,6 +165,47 @@ int ns5_batched(const float* const* m_in, float* const* o_out, const int64_t* ro
  * hp->period_k is not used. Errors as muon_step. */
 int rownorm_update(const muon_matrix* mats, int32_t count, const muon_hparams* hp,
                    void* workspace, size_t workspace_bytes, float* update_rms, void* stream);
+
+/* ---- AdamW companion for the parameters Muon does not take -------------------------
+ * "Scaling Muon for Diffusion Transformers" (setup paragraph) keeps biases,
+ * normalisation parameters and everything outside the transformer blocks on AdamW,
+ * an auxiliary group at lr 1e-4; "Muon is Scalable for LLM Training" (Sec. 2.2,
+ * matching-update-RMS paragraph) pairs Muon with AdamW for non-matrix parameters.
+ * The pages do not restate AdamW; this is Adam with bias-corrected moments and
+ * decoupled weight decay in Eq. 3's form, at 0-based step s (t = s + 1):
+ *   m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2
+ *   W <- W - lr (m / (1 - b1^t) / (sqrt(v / (1 - b2^t)) + eps) + wd W)
+ * adamw_default_hparams(): lr 1e-4 (the DiT paper's auxiliary group), beta1 0.9,
+ * beta2 0.999, eps 1e-8 (PyTorch's AdamW defaults), weight_decay 0.1 (shared with Muon). */
+typedef struct adamw_hparams {
+    float lr;
+    float beta1, beta2; /* in [0, 1) */
+    float eps;          /* > 0 */
+    float weight_decay;
+} adamw_hparams;
+
+/* One parameter tensor of any shape, as `numel` contiguous fp32 elements. w, m
+ * (first moment), v (second moment) are DEVICE pointers updated in place (zeros at
+ * s = 0); g is read only. All four 16-byte aligned; numel == 0 entries are skipped. */
+typedef struct adamw_param {
+    int64_t numel;
+    float* w;
+    float* m;
+    float* v;
+    const float* g;
+} adamw_param;
+
+/* Fills *hp with the defaults above. Host only; hp NULL is ignored. */
+void adamw_default_hparams(adamw_hparams* hp);
+
+/* One AdamW step at 0-based step `step` for `count` tensors (host array of
+ * descriptors), enqueued on `stream`: one launch per 48 tensors, 28 bytes of HBM
+ * traffic per element. fp32 throughout; no workspace.
+ * Errors: INVALID_ARG (NULL hp / params / pointers, count < 0, numel < 0, step < 0,
+ * beta outside [0, 1), eps <= 0, non-finite lr or wd), ALIGN, ALIAS (any two of all
+ * w, m, v, g ranges overlap), TOO_LARGE (numel above 2^40), HIP. */
+int adamw_step(const adamw_param* params, int32_t count, const adamw_hparams* hp, int64_t step,
+               void* stream);
 
 /* Optional per-kernel-class timing. While enabled (enable != 0), every kernel the
  * library enqueues is bracketed by HIP events recorded on the caller's stream.

@@ -8,9 +8,12 @@ from .binding import (  # noqa: F401
     SCALE_HIDDEN,
     SCALE_MAX_DIM,
     SCALE_RMS,
+    AdamWHParams,
     MuonError,
     MuonHParams,
     MuonOptimizer,
+    adamw_default_hparams,
+    adamw_step,
     default_hparams,
     load_library,
     make_workspace,

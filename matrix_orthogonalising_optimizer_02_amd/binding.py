@@ -27,11 +27,11 @@ SCALE_RMS = 2       # 0.2 / RMS(O), Eq. 6
 
 KCLASS_NAMES = ("cast", "frob", "gram", "poly", "apply", "apply_final", "rownorm_rows",
                 "colnorm_partial", "colnorm_finalize", "colnorm_apply", "rms_finalize",
-                "scaled_update")
+                "scaled_update", "adamw")
 
 EXPORTED = ("muon_abi_version", "muon_status_str", "muon_last_error", "muon_default_hparams",
             "muon_workspace_bytes", "muon_step", "ns5_batched", "rownorm_update",
-            "muon_timing_enable", "muon_timing_read")
+            "adamw_default_hparams", "adamw_step", "muon_timing_enable", "muon_timing_read")
 
 
 class MuonHParams(ctypes.Structure):
@@ -47,6 +47,16 @@ class MuonHParams(ctypes.Structure):
 class MuonMatrix(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("w", ctypes.c_void_p),
                 ("m", ctypes.c_void_p), ("g", ctypes.c_void_p)]
+
+
+class AdamWHParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float)]
+
+
+class AdamWParam(ctypes.Structure):
+    _fields_ = [("numel", ctypes.c_int64), ("w", ctypes.c_void_p), ("m", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("g", ctypes.c_void_p)]
 
 
 class MuonError(RuntimeError):
@@ -83,9 +93,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ns5_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_int64),
                                 ctypes.POINTER(ctypes.c_int64), i32, ctypes.POINTER(MuonHParams), vp, sz, vp]
     lib.rownorm_update.argtypes = [ctypes.POINTER(MuonMatrix), i32, ctypes.POINTER(MuonHParams), vp, sz, vp, vp]
+    lib.adamw_default_hparams.argtypes = [ctypes.POINTER(AdamWHParams)]
+    lib.adamw_default_hparams.restype = None
+    lib.adamw_step.argtypes = [ctypes.POINTER(AdamWParam), i32, ctypes.POINTER(AdamWHParams), i64, vp]
     lib.muon_timing_enable.argtypes = [ctypes.c_int]
     lib.muon_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
-    for name in ("muon_step", "ns5_batched", "rownorm_update", "muon_workspace_bytes",
+    for name in ("muon_step", "ns5_batched", "rownorm_update", "muon_workspace_bytes", "adamw_step",
                  "muon_timing_enable", "muon_timing_read"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
@@ -240,6 +253,46 @@ def ns5_batched(inputs, outputs=None, hp: Optional[MuonHParams] = None, workspac
                                     _stream_handle(stream, dev))
     _check(rc, "ns5_batched")
     return outputs
+
+
+def adamw_default_hparams(**overrides) -> AdamWHParams:
+    hp = AdamWHParams()
+    load_library().adamw_default_hparams(ctypes.byref(hp))
+    for k, v in overrides.items():
+        if not hasattr(hp, k):
+            raise KeyError(k)
+        setattr(hp, k, v)
+    return hp
+
+
+def _check_flat(t, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor")
+    if t.numel() and t.device.type != "cuda":
+        raise ValueError(f"{name} must live on a GPU")
+
+
+def adamw_step(params, grads, exp_avgs, exp_avg_sqs, step: int, hp: Optional[AdamWHParams] = None,
+               stream=None):
+    """One AdamW step (0-based `step`) over tensors of any shape, in place."""
+    hp = hp or adamw_default_hparams()
+    n = len(params)
+    if not (n == len(grads) == len(exp_avgs) == len(exp_avg_sqs)):
+        raise ValueError("params, grads and moment lists must have the same length")
+    arr = (AdamWParam * max(n, 1))()
+    for i, (w, g, m, v) in enumerate(zip(params, grads, exp_avgs, exp_avg_sqs)):
+        for t, nm in ((w, "param"), (g, "grad"), (m, "exp_avg"), (v, "exp_avg_sq")):
+            _check_flat(t, f"{nm}[{i}]")
+        if not (w.shape == g.shape == m.shape == v.shape):
+            raise ValueError(f"shape mismatch at index {i}")
+        arr[i] = AdamWParam(w.numel(), w.data_ptr() or None, m.data_ptr() or None, v.data_ptr() or None,
+                            g.data_ptr() or None)
+    dev = params[0].device if params else None
+    rc = load_library().adamw_step(arr, n, ctypes.byref(hp), int(step), _stream_handle(stream, dev))
+    _check(rc, "adamw_step")
 
 
 def timing_enable(enable: bool = True):

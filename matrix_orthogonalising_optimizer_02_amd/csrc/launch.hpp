@@ -159,6 +159,33 @@ struct UpdArgs {
 
 constexpr int kUpdBlockElems = 4096;
 
+// ---- AdamW for the hybrid optimizer's non-matrix parameters ---------------------
+// Tensors of any shape as flat fp32 arrays; 4096 elements per block; descriptors of
+// up to kAdamMaxTensors tensors travel in the kernel arguments.
+struct AdamDesc {
+    float* w;
+    float* m;
+    float* v;
+    const float* g;
+    int64_t n;
+    int32_t blk_begin;     // first block of this tensor in the launch
+    int32_t pad_;
+};
+
+constexpr int kAdamMaxTensors = 48;
+constexpr int kAdamBlockElems = 4096;
+
+struct AdamArgs {
+    AdamDesc d[kAdamMaxTensors];
+    int32_t n;
+    int32_t total;
+    float beta1, beta2, one_minus_beta1, one_minus_beta2;
+    float eps;
+    float decay;           // 1 - lr * weight_decay
+    float lr_bc1;          // lr / (1 - beta1^t)
+    float inv_sqrt_bc2;    // 1 / sqrt(1 - beta2^t)
+};
+
 constexpr int kColChunkRows = 256;
 constexpr int kColTileCols = 256;
 // Rows up to this length keep M' in registers (one 256-thread block per row).
@@ -174,6 +201,7 @@ hipError_t launch_colnorm_partial(const ColArgs& a, bool vec, hipStream_t s);
 hipError_t launch_colnorm_finalize(const ColArgs& a, int fin_total, hipStream_t s);
 hipError_t launch_colnorm_apply(const ColArgs& a, bool vec, hipStream_t s);
 hipError_t launch_rms_finalize(const RmsArgs& a, hipStream_t s);
+hipError_t launch_adamw(const AdamArgs& a, hipStream_t s);
 hipError_t launch_scaled_update(const UpdArgs& a, hipStream_t s);
 
 // GEMM block tiles (host-side tile counting must match the kernels).

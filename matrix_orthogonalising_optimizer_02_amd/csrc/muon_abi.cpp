@@ -710,6 +710,87 @@ MUON_API int rownorm_update(const muon_matrix* mats, int32_t count, const muon_h
     return do_rownorm(mats, count, hp, workspace, workspace_bytes, update_rms, stream, false);
 }
 
+MUON_API void adamw_default_hparams(adamw_hparams* hp) {
+    if (!hp) return;
+    hp->lr = 1e-4f;
+    hp->beta1 = 0.9f;
+    hp->beta2 = 0.999f;
+    hp->eps = 1e-8f;
+    hp->weight_decay = 0.1f;
+}
+
+MUON_API int adamw_step(const adamw_param* params, int32_t count, const adamw_hparams* hp, int64_t step,
+                        void* stream) {
+    g_last_error.clear();
+    if (!hp) return fail(MUON_ERR_INVALID_ARG, "hparams is NULL");
+    if (!std::isfinite(hp->lr) || !std::isfinite(hp->weight_decay))
+        return fail(MUON_ERR_INVALID_ARG, "lr and weight_decay must be finite");
+    if (!(hp->beta1 >= 0.f && hp->beta1 < 1.f) || !(hp->beta2 >= 0.f && hp->beta2 < 1.f))
+        return fail(MUON_ERR_INVALID_ARG, "beta1 and beta2 must be in [0, 1)");
+    if (!(hp->eps > 0.f) || !std::isfinite(hp->eps)) return fail(MUON_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (step < 0) return fail(MUON_ERR_INVALID_ARG, "step < 0");
+    if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count < 0");
+    if (count > 0 && !params) return fail(MUON_ERR_INVALID_ARG, "params is NULL");
+    std::vector<Range> ranges;
+    for (int i = 0; i < count; ++i) {
+        const adamw_param& p = params[i];
+        if (p.numel < 0) return fail(MUON_ERR_INVALID_ARG, "negative numel at index " + std::to_string(i));
+        if (p.numel == 0) continue;
+        if (p.numel > kMaxElems) return fail(MUON_ERR_TOO_LARGE, "tensor " + std::to_string(i) + " above 2^40 elements");
+        if (!p.w || !p.m || !p.v || !p.g) return fail(MUON_ERR_INVALID_ARG, "NULL pointer at index " + std::to_string(i));
+        if (!aligned16(p.w) || !aligned16(p.m) || !aligned16(p.v) || !aligned16(p.g))
+            return fail(MUON_ERR_ALIGN, "tensor pointer not 16-byte aligned at index " + std::to_string(i));
+        const uintptr_t bytes = uintptr_t(p.numel) * 4;
+        ranges.push_back({reinterpret_cast<uintptr_t>(p.w), reinterpret_cast<uintptr_t>(p.w) + bytes, true});
+        ranges.push_back({reinterpret_cast<uintptr_t>(p.m), reinterpret_cast<uintptr_t>(p.m) + bytes, true});
+        ranges.push_back({reinterpret_cast<uintptr_t>(p.v), reinterpret_cast<uintptr_t>(p.v) + bytes, true});
+        ranges.push_back({reinterpret_cast<uintptr_t>(p.g), reinterpret_cast<uintptr_t>(p.g) + bytes, false});
+    }
+    int rc = check_overlaps(ranges);
+    if (rc) return rc;
+    // bias corrections in double on the host (t = step + 1)
+    const double t = double(step) + 1.0;
+    const double bc1 = 1.0 - std::pow(double(hp->beta1), t);
+    const double bc2 = 1.0 - std::pow(double(hp->beta2), t);
+    AdamArgs a{};
+    a.beta1 = hp->beta1;
+    a.beta2 = hp->beta2;
+    a.one_minus_beta1 = float(1.0 - double(hp->beta1));
+    a.one_minus_beta2 = float(1.0 - double(hp->beta2));
+    a.eps = hp->eps;
+    a.decay = float(1.0 - double(hp->lr) * double(hp->weight_decay));
+    a.lr_bc1 = float(double(hp->lr) / bc1);
+    a.inv_sqrt_bc2 = float(1.0 / std::sqrt(bc2));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int64_t blocks = 0;
+    auto flush = [&]() -> int {
+        if (a.n == 0) return MUON_OK;
+        a.total = int32_t(blocks);
+        const int r = run_kernel(MUON_KCLASS_ADAMW, s, "adamw", [&] { return launch_adamw(a, s); });
+        a.n = 0;
+        blocks = 0;
+        return r;
+    };
+    for (int i = 0; i < count; ++i) {
+        const adamw_param& p = params[i];
+        if (p.numel == 0) continue;
+        const int64_t nb = (p.numel + kAdamBlockElems - 1) / kAdamBlockElems;
+        if (a.n == kAdamMaxTensors || blocks + nb >= (int64_t(1) << 31)) {
+            rc = flush();
+            if (rc) return rc;
+        }
+        AdamDesc& d = a.d[a.n++];
+        d.w = p.w;
+        d.m = p.m;
+        d.v = p.v;
+        d.g = p.g;
+        d.n = p.numel;
+        d.blk_begin = int32_t(blocks);
+        blocks += nb;
+    }
+    return flush();
+}
+
 MUON_API int muon_timing_enable(int enable) {
     g_last_error.clear();
     std::lock_guard<std::mutex> lk(g_timing.mu);

@@ -244,3 +244,46 @@ def test_timing_toggle_without_launches(lib):
 def test_product_path_refuses_without_library(tmp_path):
     with pytest.raises(RuntimeError):
         B.load_library(str(tmp_path / "missing.so"))
+
+
+# ---------------------------------------------------------------- AdamW ----
+
+def test_adamw_defaults_match_the_oracle_reading(lib):
+    from oracle import adamw_oracle as A
+    hp, ref = B.adamw_default_hparams(), A.AdamWHParams()
+    for f in ("lr", "beta1", "beta2", "eps", "weight_decay"):
+        assert getattr(hp, f) == pytest.approx(getattr(ref, f), rel=1e-6), f
+
+
+def adam_params(specs):
+    arr = (B.AdamWParam * max(len(specs), 1))()
+    for i, (n, w, m, v, g) in enumerate(specs):
+        arr[i] = B.AdamWParam(n, w, m, v, g)
+    return arr
+
+
+@fake_only
+def test_adamw_argument_errors(lib):
+    span = 1 << 32
+    ok = (1000, BASE, BASE + span, BASE + 2 * span, BASE + 3 * span)
+    hp = B.adamw_default_hparams()
+    call = lambda arr, n, h=hp, step=0: lib.adamw_step(arr, n, ctypes.byref(h) if h is not None else None, step, None)
+    assert call(None, 0) == B.MUON_OK
+    assert call(adam_params([(0, None, None, None, None)]), 1) == B.MUON_OK
+    assert call(adam_params([ok]), 1, h=None) == B.MUON_ERR_INVALID_ARG
+    for field, val in (("beta1", 1.0), ("beta2", -0.1), ("eps", 0.0), ("lr", float("nan")),
+                       ("weight_decay", float("inf"))):
+        assert call(adam_params([ok]), 1, h=B.adamw_default_hparams(**{field: val})) == B.MUON_ERR_INVALID_ARG, field
+    assert call(adam_params([ok]), 1, step=-1) == B.MUON_ERR_INVALID_ARG
+    assert call(adam_params([ok]), -1) == B.MUON_ERR_INVALID_ARG
+    assert call(None, 1) == B.MUON_ERR_INVALID_ARG
+    assert call(adam_params([(-5,) + ok[1:]]), 1) == B.MUON_ERR_INVALID_ARG
+    assert call(adam_params([(1000, None) + ok[2:]]), 1) == B.MUON_ERR_INVALID_ARG
+    assert call(adam_params([(1 << 41,) + ok[1:]]), 1) == B.MUON_ERR_TOO_LARGE
+    assert call(adam_params([(1000, BASE + 4) + ok[2:]]), 1) == B.MUON_ERR_ALIGN
+    # m aliasing w, g inside v, two tensors sharing a second moment
+    assert call(adam_params([(1000, BASE, BASE, BASE + 2 * span, BASE + 3 * span)]), 1) == B.MUON_ERR_ALIAS
+    assert call(adam_params([(1000, BASE, BASE + span, BASE + 2 * span, BASE + 2 * span + 64)]), 1) == B.MUON_ERR_ALIAS
+    other = (1000, BASE + 4 * span, BASE + 5 * span, BASE + 2 * span, BASE + 6 * span)
+    assert call(adam_params([ok, other]), 2) == B.MUON_ERR_ALIAS
+    assert lib.muon_last_error().decode() != ""
