@@ -76,6 +76,8 @@ def parse():
     ap.add_argument("--vanilla-steps", type=int, default=4)
     ap.add_argument("--variant-steps", type=int, default=2,
                     help="timed steps per scale-rule / monitor variant (0: skip)")
+    ap.add_argument("--adamw-steps", type=int, default=5,
+                    help="timed AdamW steps over the model's AdamW group (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
@@ -174,6 +176,49 @@ def measure_variants(pkg, torch, weights, momenta, grads, ws, k, wl, n, say):
     return res
 
 
+def measure_adamw(pkg, torch, dev, wl, n, say):
+    """AdamW over the AdamW group of the model whose block the workload is (biases,
+    norms, embedders, final layer), 28 bytes per element, HIP events per launch."""
+    from matrix_orthogonalising_optimizer_02_amd import hybrid as H
+    scale = {5120: "15B", 4096: "9B", 3072: "4B", 2048: "1.3B"}.get(min(min(s) for s in wl.shapes))
+    if scale is None:
+        return None
+    h, depth = H.DIT_SCALES[scale]
+    pl = H.dit_parameter_list(h, depth)
+    _, adamw_names = H.split_param_groups(pl)
+    shapes = dict(pl)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    w = [torch.zeros(shapes[nm], dtype=torch.float32, device=dev) for nm in adamw_names]
+    gr = [torch.empty(shapes[nm], dtype=torch.float32, device=dev).normal_(0.0, 1e-3, generator=g) for nm in adamw_names]
+    m = [torch.zeros_like(x) for x in w]
+    v = [torch.zeros_like(x) for x in w]
+    elems = sum(x.numel() for x in w)
+    group = pkg.AdamWGroup(w, gr, m, v)
+    group.step(0)
+    torch.cuda.synchronize()
+    pkg.timing_enable(True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for s in range(n):
+        group.step(s + 1)
+    b.record()
+    torch.cuda.synchronize()
+    kern = pkg.timing_read()
+    pkg.timing_enable(False)
+    step_ms = a.elapsed_time(b) / n
+    kms, launches = kern["adamw"]
+    mu, ad = H.count_params(pl)
+    res = {"model": f"double-stream DiT {scale} (H={h}, {depth} blocks, {(mu + ad) / 1e9:.2f} B parameters)",
+           "muon_share": round(mu / (mu + ad), 4), "adamw_tensors": len(w), "adamw_elements": elems,
+           "adamw_step_ms": round(step_ms, 4), "adamw_launches_per_step": launches // n,
+           "adamw_kernel_gbs": round(28.0 * elems / (kms / n * 1e-3) / 1e9, 1),
+           "adamw_step_gbs": round(28.0 * elems / (step_ms * 1e-3) / 1e9, 1)}
+    say(f"hybrid: {res}")
+    del w, gr, m, v
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -254,6 +299,7 @@ def main():
 
     variants = measure_variants(pkg, torch, weights, momenta, grads, ws, k, wl, args.variant_steps, say) \
         if args.variant_steps > 0 else None
+    hybrid = measure_adamw(pkg, torch, dev, wl, args.adamw_steps, say) if args.adamw_steps > 0 else None
 
     refreshes = args.steps
     rownorm_steps = args.steps * (k - 1)
@@ -326,6 +372,8 @@ def main():
     }
     if variants is not None:
         out["variants"] = variants
+    if hybrid is not None:
+        out["hybrid"] = hybrid
     if not args.no_cpu_baseline:
         say("cpu baseline: timing the float64 oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(wl, k)

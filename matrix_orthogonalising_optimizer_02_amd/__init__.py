@@ -8,6 +8,7 @@ from .binding import (  # noqa: F401
     SCALE_HIDDEN,
     SCALE_MAX_DIM,
     SCALE_RMS,
+    AdamWGroup,
     AdamWHParams,
     MuonError,
     MuonHParams,

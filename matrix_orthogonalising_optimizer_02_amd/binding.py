@@ -275,24 +275,52 @@ def _check_flat(t, name):
         raise ValueError(f"{name} must live on a GPU")
 
 
+class AdamWGroup:
+    """Tensors for repeated AdamW steps, with the C descriptor array built once.
+
+    The gradient tensors given here are read at every step (write each step's gradients
+    into them in place), unless step() is passed a new list.
+    """
+
+    def __init__(self, params, grads, exp_avgs, exp_avg_sqs, hp: Optional[AdamWHParams] = None):
+        n = len(params)
+        if not (n == len(grads) == len(exp_avgs) == len(exp_avg_sqs)):
+            raise ValueError("params, grads and moment lists must have the same length")
+        self.hp = hp or adamw_default_hparams()
+        self.tensors = (list(params), list(grads), list(exp_avgs), list(exp_avg_sqs))
+        self.arr = (AdamWParam * max(n, 1))()
+        for i, (w, g, m, v) in enumerate(zip(params, grads, exp_avgs, exp_avg_sqs)):
+            for t, nm in ((w, "param"), (g, "grad"), (m, "exp_avg"), (v, "exp_avg_sq")):
+                _check_flat(t, f"{nm}[{i}]")
+            if not (w.shape == g.shape == m.shape == v.shape):
+                raise ValueError(f"shape mismatch at index {i}")
+            self.arr[i] = AdamWParam(w.numel(), w.data_ptr() or None, m.data_ptr() or None,
+                                     v.data_ptr() or None, g.data_ptr() or None)
+        self.n = n
+        self.device = params[0].device if params else None
+
+    def set_grads(self, grads):
+        if len(grads) != self.n:
+            raise ValueError("one gradient per parameter")
+        for i, (g, w) in enumerate(zip(grads, self.tensors[0])):
+            _check_flat(g, f"grad[{i}]")
+            if g.shape != w.shape:
+                raise ValueError(f"shape mismatch at index {i}")
+            self.arr[i].g = g.data_ptr() or None
+        self.tensors = (self.tensors[0], list(grads), self.tensors[2], self.tensors[3])
+
+    def step(self, step: int, stream=None, grads=None):
+        if grads is not None:
+            self.set_grads(grads)
+        rc = load_library().adamw_step(self.arr, self.n, ctypes.byref(self.hp), int(step),
+                                       _stream_handle(stream, self.device))
+        _check(rc, "adamw_step")
+
+
 def adamw_step(params, grads, exp_avgs, exp_avg_sqs, step: int, hp: Optional[AdamWHParams] = None,
                stream=None):
     """One AdamW step (0-based `step`) over tensors of any shape, in place."""
-    hp = hp or adamw_default_hparams()
-    n = len(params)
-    if not (n == len(grads) == len(exp_avgs) == len(exp_avg_sqs)):
-        raise ValueError("params, grads and moment lists must have the same length")
-    arr = (AdamWParam * max(n, 1))()
-    for i, (w, g, m, v) in enumerate(zip(params, grads, exp_avgs, exp_avg_sqs)):
-        for t, nm in ((w, "param"), (g, "grad"), (m, "exp_avg"), (v, "exp_avg_sq")):
-            _check_flat(t, f"{nm}[{i}]")
-        if not (w.shape == g.shape == m.shape == v.shape):
-            raise ValueError(f"shape mismatch at index {i}")
-        arr[i] = AdamWParam(w.numel(), w.data_ptr() or None, m.data_ptr() or None, v.data_ptr() or None,
-                            g.data_ptr() or None)
-    dev = params[0].device if params else None
-    rc = load_library().adamw_step(arr, n, ctypes.byref(hp), int(step), _stream_handle(stream, dev))
-    _check(rc, "adamw_step")
+    AdamWGroup(params, grads, exp_avgs, exp_avg_sqs, hp).step(step, stream)
 
 
 def timing_enable(enable: bool = True):

@@ -118,6 +118,7 @@ class HybridOptimizer:
         dev = next(iter(named_params.values())).device if named_params else "cuda"
         self.workspace = B.make_workspace([tuple(named_params[n].shape) for n in self.muon_names], dev) \
             if self.muon_names else None
+        self._adamw = None  # descriptor array, built at the first step
         self.step_count = 0
 
     def step(self, grads: Dict[str, "object"], stream=None, update_rms=None):
@@ -126,9 +127,15 @@ class HybridOptimizer:
                         [grads[n] for n in self.muon_names], self.step_count, self.muon_hp, self.workspace,
                         stream, update_rms)
         if self.adamw_names:
-            B.adamw_step([self.params[n] for n in self.adamw_names], [grads[n] for n in self.adamw_names],
-                         [self.exp_avg[n] for n in self.adamw_names], [self.exp_avg_sq[n] for n in self.adamw_names],
-                         self.step_count, self.adamw_hp, stream)
+            g = [grads[n] for n in self.adamw_names]
+            if self._adamw is None:
+                self._adamw = B.AdamWGroup([self.params[n] for n in self.adamw_names], g,
+                                           [self.exp_avg[n] for n in self.adamw_names],
+                                           [self.exp_avg_sq[n] for n in self.adamw_names], self.adamw_hp)
+                self._adamw.step(self.step_count, stream)
+            else:
+                same = all(a is b for a, b in zip(g, self._adamw.tensors[1]))
+                self._adamw.step(self.step_count, stream, None if same else g)
         self.step_count += 1
 
     def state_dict(self):
