@@ -63,7 +63,15 @@ struct GemmCfg {
     static constexpr int kEpiF32 = (HN * (WM + 4) > WM * (HN + 4) ? HN * (WM + 4) : WM * (HN + 4)) * 4;
     static constexpr int kEpiWave = ((kEpiBf16 > kEpiF32 ? kEpiBf16 : kEpiF32) + 15) / 16 * 16;
     static constexpr int kMainBytes = STAGES * (BM + BN) * BK * 2;
-    static constexpr int kLdsBytes = kMainBytes > 4 * kEpiWave ? kMainBytes : 4 * kEpiWave;
+    // K-major operand tiles (rows k of BM = 256 columns, read with ds_read_b64_tr_b16):
+    // a 1 KiB wave-wide load fills one slot with rows k and k + 4; slots are padded to
+    // 1088 bytes; 16 slots hold the 32 rows of a K step.
+    static constexpr bool kTrOK = kDirect && BK == 32 && BM == 256 && BN == 256;
+    static constexpr int kTrSlot = 544;            // elements per slot (1024 + 64 bytes)
+    static constexpr int kTrStage = 16 * kTrSlot;  // elements per operand per stage
+    static constexpr int kMainBytesTr = kTrOK ? STAGES * 2 * kTrStage * 2 : 0;
+    static constexpr int kMainMax = kMainBytes > kMainBytesTr ? kMainBytes : kMainBytesTr;
+    static constexpr int kLdsBytes = kMainMax > 4 * kEpiWave ? kMainMax : 4 * kEpiWave;
     static_assert(BK == 32 || BK == 64, "K step");
     static_assert(kDirect || STAGES == 2, "the register-staged path is double-buffered");
 };
@@ -74,6 +82,26 @@ struct GemmCfg {
 template <class Cfg>
 __device__ __forceinline__ int gemm_swz(int row, int chunk) {
     return row * Cfg::BK + ((chunk ^ ((row >> Cfg::SWS) & (Cfg::CPR - 1))) << 3);
+}
+
+// K-major tile: row k of a K step lives in slot (k & 3) + 4 (k >> 3), half (k >> 2) & 1
+// (slot = 1 KiB load + 64 bytes of padding). The four rows k, k + 1, k + 2, k + 3 that
+// one 32-lane half of a transposing read touches sit in four consecutive slots, i.e. in
+// four different 64-byte bank windows, and every offset is a sum of a per-lane term
+// and compile-time terms.
+template <class Cfg>
+__device__ __forceinline__ int tr_off(int k, int col) {
+    return ((k & 3) + 4 * (k >> 3)) * Cfg::kTrSlot + ((k >> 2) & 1) * 256 + col;
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+// ds_read_b64_tr_b16 on gfx950: within each group of 16 lanes, output lane 4q + r
+// receives element r of the 8-byte chunks addressed by lanes q, q + 4, q + 8, q + 12
+// (in that order): a 16 x 4 block of 16-bit values is transposed across the group.
+__device__ __forceinline__ v4i16 lds_read_tr16(const unsigned short* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
 }
 
 template <bool B>
@@ -142,10 +170,16 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
 
 template <int MODE, class Cfg>
-__device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short* sA, unsigned short* sB) {
+__device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short* smem) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::NT;
     constexpr int WM = Cfg::WM, WN = Cfg::WN, TM = Cfg::TM, TN = Cfg::TN;
-    constexpr int STAGE_A = BM * BK, STAGE_B = BN * BK;
+    // The big Gram reads both operands from X_c ([n_p, m_p], K = n along its rows):
+    // K-major tiles and transposing fragment reads. Every other stage reads K-contiguous
+    // rows (the small Gram from X_r).
+    constexpr bool kTr = (MODE == kModeGram) && Cfg::kTrOK;
+    constexpr int STAGE_A = kTr ? Cfg::kTrStage : BM * BK, STAGE_B = kTr ? Cfg::kTrStage : BN * BK;
+    unsigned short* const sA = smem;
+    unsigned short* const sB = smem + Cfg::STAGES * STAGE_A;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -182,11 +216,12 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
     const unsigned short* Q;
     int64_t ld;
     int K;
-    if constexpr (MODE == kModeGram) { P = d.xr; Q = d.xr; ld = d.n_p; K = d.n_p; }
+    if constexpr (kTr) { P = d.xc; Q = d.xc; ld = d.m_p; K = d.n_p; }
+    else if constexpr (MODE == kModeGram) { P = d.xr; Q = d.xr; ld = d.n_p; K = d.n_p; }
     else if constexpr (MODE == kModePoly) { P = d.a; Q = d.a; ld = d.m_p; K = d.m_p; }
     else { P = d.b; Q = d.xc; ld = d.m_p; K = d.m_p; }
-    const unsigned short* Pt = P + (int64_t)ti * BM * ld;
-    const unsigned short* Qt = Q + (int64_t)tj * BN * ld;
+    const unsigned short* Pt = kTr ? P + (int64_t)ti * BM : P + (int64_t)ti * BM * ld;
+    const unsigned short* Qt = kTr ? Q + (int64_t)tj * BN : Q + (int64_t)tj * BN * ld;
 
     floatx16 acc[TM][TN];
 #pragma unroll
@@ -206,44 +241,89 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         constexpr int LOADS = Cfg::IA + Cfg::IB;  // wave-wide loads per K step
         constexpr int KK = BK / 16;               // MFMA sub-steps per K step
         constexpr int NMF = TM * TN;              // MFMAs per sub-step
-        constexpr int NFR = TM + TN;              // fragment reads per sub-step
+        // LDS reads per sub-step: one 16-byte read per fragment, or two transposing
+        // 8-byte reads (k 0-3 and 4-7 of the lane's 8) for K-major tiles
+        constexpr int NFR = kTr ? 2 * (TM + TN) : TM + TN;
         constexpr int LPS = (LOADS + KK - 2) / (KK - 1);  // global loads per sub-step
         static_assert(KK >= 2 && KK % 2 == 0, "sub-step parity must restart at 0 every K step");
         static_assert(NFR <= NMF && 2 * LPS <= NMF, "issue slots");
+        static_assert(!kTr || (Cfg::IA == 4 && Cfg::IB == 4), "K-major tiles: 16 loads of two rows each");
         // the wave index is uniform: keep it scalar so the LDS destinations (M0) are too
         const int swave = __builtin_amdgcn_readfirstlane(wave);
         const int lrow = lane / CPR, lpc = lane % CPR;
         int64_t offa[Cfg::IA], offb[Cfg::IB];
 #pragma unroll
         for (int q = 0; q < Cfg::IA; ++q) {
-            const int row = (swave * Cfg::IA + q) * RPI + lrow;
-            offa[q] = (int64_t)row * ld + ((lpc ^ ((row >> Cfg::SWS) & (CPR - 1))) << 3);
+            if constexpr (kTr) {  // slot s: rows (s & 3) + 8 (s >> 2) and that + 4
+                const int sl = swave * Cfg::IA + q;
+                const int row = (sl & 3) + 8 * (sl >> 2) + 4 * (lane >> 5);
+                offa[q] = (int64_t)row * ld + ((lane & 31) << 3);
+            } else {
+                const int row = (swave * Cfg::IA + q) * RPI + lrow;
+                offa[q] = (int64_t)row * ld + ((lpc ^ ((row >> Cfg::SWS) & (CPR - 1))) << 3);
+            }
         }
 #pragma unroll
         for (int q = 0; q < Cfg::IB; ++q) {
-            const int row = (swave * Cfg::IB + q) * RPI + lrow;
-            offb[q] = (int64_t)row * ld + ((lpc ^ ((row >> Cfg::SWS) & (CPR - 1))) << 3);
+            if constexpr (kTr) {
+                const int sl = swave * Cfg::IB + q;
+                const int row = (sl & 3) + 8 * (sl >> 2) + 4 * (lane >> 5);
+                offb[q] = (int64_t)row * ld + ((lane & 31) << 3);
+            } else {
+                const int row = (swave * Cfg::IB + q) * RPI + lrow;
+                offb[q] = (int64_t)row * ld + ((lpc ^ ((row >> Cfg::SWS) & (CPR - 1))) << 3);
+            }
         }
-        auto gload = [&](int buf, int k0, int idx) {  // idx < LOADS: one 1 KiB load
+        // one 1 KiB load (idx < LOADS) into the stage whose A and B tiles start at dA, dB
+        auto gload = [&](unsigned short* dA, unsigned short* dB, int k0, int idx) {
+            const int64_t kofs = kTr ? (int64_t)k0 * ld : (int64_t)k0;
+            constexpr int SLOT = kTr ? Cfg::kTrSlot : 512;
             if (idx < Cfg::IA)
-                __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Pt + offa[idx] + k0),
-                                                 (lds_ptr_t)(sA + buf * STAGE_A + (swave * Cfg::IA + idx) * 512),
-                                                 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Pt + offa[idx] + kofs),
+                                                 (lds_ptr_t)(dA + (swave * Cfg::IA + idx) * SLOT), 16, 0, 0);
             else
-                __builtin_amdgcn_global_load_lds(
-                    (gbl_ptr_t)(Qt + offb[idx - Cfg::IA] + k0),
-                    (lds_ptr_t)(sB + buf * STAGE_B + (swave * Cfg::IB + idx - Cfg::IA) * 512), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Qt + offb[idx - Cfg::IA] + kofs),
+                                                 (lds_ptr_t)(dB + (swave * Cfg::IB + idx - Cfg::IA) * SLOT), 16, 0, 0);
         };
-        // Fragments are double-buffered in registers.
+        // Fragments are double-buffered in registers (K-major tiles: as two halves).
         bf16x8 fa[2][TM], fb[2][TN];
-        auto frag = [&](int fbuf, int stage, int kk, int r) {  // r < NFR: one 16-byte read
-            const int ch = kk * 2 + (lane >> 5);
-            if (r < TM)
-                fa[fbuf][r] = *reinterpret_cast<const bf16x8*>(
-                    sA + stage * STAGE_A + gemm_swz<Cfg>(wm * WM + r * 32 + (lane & 31), ch));
+        v4i16 fah[2][TM][2], fbh[2][TN][2];
+        // one LDS read (r < NFR) of sub-step kk from the stage whose tiles start at cA, cB
+        auto frag = [&](int fbuf, const unsigned short* cA, const unsigned short* cB, int kk, int r) {
+            if constexpr (kTr) {
+                // lane l addresses row k = 16 kk + 8 (l / 32) + 4 h + (l / 4) % 4 at column
+                // 16 ((l / 16) % 2) + 4 (l % 4) of the fragment's 32 columns; after the
+                // transposing read it holds column l % 32, k = 16 kk + 8 (l / 32) + 4 h + 0..3
+                const int f = r >> 1, h = r & 1;
+                const int k = kk * 16 + ((lane >> 5) << 3) + (h << 2) + ((lane >> 2) & 3);
+                const int c = (((lane >> 4) & 1) << 4) + ((lane & 3) << 2);
+                if (f < TM)
+                    fah[fbuf][f][h] = lds_read_tr16(cA + tr_off<Cfg>(k, wm * WM + f * 32 + c));
+                else
+                    fbh[fbuf][f - TM][h] = lds_read_tr16(cB + tr_off<Cfg>(k, wn * WN + (f - TM) * 32 + c));
+            } else {
+                const int ch = kk * 2 + (lane >> 5);
+                if (r < TM)
+                    fa[fbuf][r] = *reinterpret_cast<const bf16x8*>(
+                        cA + gemm_swz<Cfg>(wm * WM + r * 32 + (lane & 31), ch));
+                else
+                    fb[fbuf][r - TM] = *reinterpret_cast<const bf16x8*>(
+                        cB + gemm_swz<Cfg>(wn * WN + (r - TM) * 32 + (lane & 31), ch));
+            }
+        };
+        auto opa = [&](int fbuf, int a) -> bf16x8 {
+            if constexpr (kTr)
+                return __builtin_bit_cast(bf16x8, __builtin_shufflevector(fah[fbuf][a][0], fah[fbuf][a][1],
+                                                                          0, 1, 2, 3, 4, 5, 6, 7));
             else
-                fb[fbuf][r - TM] = *reinterpret_cast<const bf16x8*>(
-                    sB + stage * STAGE_B + gemm_swz<Cfg>(wn * WN + (r - TM) * 32 + (lane & 31), ch));
+                return fa[fbuf][a];
+        };
+        auto opb = [&](int fbuf, int b) -> bf16x8 {
+            if constexpr (kTr)
+                return __builtin_bit_cast(bf16x8, __builtin_shufflevector(fbh[fbuf][b][0], fbh[fbuf][b][1],
+                                                                          0, 1, 2, 3, 4, 5, 6, 7));
+            else
+                return fb[fbuf][b];
         };
         // wait until this wave's loads of K step `st` are complete, given that steps
         // up to `last_issued` have been issued (loads complete in issue order)
@@ -256,11 +336,11 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         for (int st = 0; st < STAGES - 1; ++st)
             if (st < nk)
 #pragma unroll
-                for (int idx = 0; idx < LOADS; ++idx) gload(st, st * BK, idx);
+                for (int idx = 0; idx < LOADS; ++idx) gload(sA + st * STAGE_A, sB + st * STAGE_B, st * BK, idx);
         wait_step(0, min(STAGES - 2, nk - 1));
         barrier_no_fence();
 #pragma unroll
-        for (int r = 0; r < NFR; ++r) frag(0, 0, 0, r);
+        for (int r = 0; r < NFR; ++r) frag(0, sA, sB, 0, r);
         // Main loop. Each MFMA occupies the matrix pipe for 8 passes; the wave issues at
         // most one LDS read and one global load between two MFMAs, so the other issue
         // work hides in the MFMA shadow. Sub-steps 0 .. KK-2 read the next sub-step's
@@ -269,35 +349,49 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         // the other waves at the barrier and then reads step kt + 1's first fragments.
         // MORE: this step issues global loads; NEXT: a following K step exists. Both are
         // compile-time in each instance so the unrolled body has no branches.
+        //
+        // The stage a K step loads into (kt + STAGES - 1) differs from the two it reads
+        // (kt, kt + 1) when STAGES >= 3; passing the three stages as restrict pointers
+        // tells the compiler so. Without it, a transposing LDS read after an LDS-DMA load
+        // gets a wait for every outstanding load; the explicit waits above already order
+        // each read after the loads of its own stage.
+        static_assert(STAGES >= 3, "the load stage must differ from the stages read");
         auto kstep = [&](int kt, auto more_c, auto next_c) {
             constexpr bool MORE = decltype(more_c)::value;
             constexpr bool NEXT = decltype(next_c)::value;
             const int lbuf = (kt + STAGES - 1) % STAGES, lk0 = (kt + STAGES - 1) * BK;
-            const int cur = kt % STAGES;
+            const int cur = kt % STAGES, nxt = (kt + 1) % STAGES;
             const int last_issued = min(kt + STAGES - 1, nk - 1);
+            auto body = [&](unsigned short* __restrict__ dA, unsigned short* __restrict__ dB,
+                            const unsigned short* __restrict__ cA, const unsigned short* __restrict__ cB,
+                            const unsigned short* __restrict__ nA, const unsigned short* __restrict__ nB) {
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const int fbuf = kk & 1;
-                const bool last = kk == KK - 1;
-                if (last && NEXT) {
-                    wait_lgkm0();
-                    wait_step(kt + 1, last_issued);
-                    barrier_no_fence();
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int i = 0; i < NMF; ++i) {
-                    const int a = i / TN, b = i % TN;
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fbuf][a], fb[fbuf][b], acc[a][b], 0, 0, 0);
-                    if (i < NFR) {
-                        if (!last) frag(fbuf ^ 1, cur, kk + 1, i);
-                        else if (NEXT) frag(fbuf ^ 1, (kt + 1) % STAGES, 0, i);
+                for (int kk = 0; kk < KK; ++kk) {
+                    const int fbuf = kk & 1;
+                    const bool last = kk == KK - 1;
+                    if (last && NEXT) {
+                        wait_lgkm0();
+                        wait_step(kt + 1, last_issued);
+                        barrier_no_fence();
                     }
-                    if (MORE && !last && (i & 1) && (i >> 1) < LPS && kk * LPS + (i >> 1) < LOADS)
-                        gload(lbuf, lk0, kk * LPS + (i >> 1));
                     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int i = 0; i < NMF; ++i) {
+                        const int a = i / TN, b = i % TN;
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa(fbuf, a), opb(fbuf, b), acc[a][b],
+                                                                           0, 0, 0);
+                        if (i < NFR) {
+                            if (!last) frag(fbuf ^ 1, cA, cB, kk + 1, i);
+                            else if (NEXT) frag(fbuf ^ 1, nA, nB, 0, i);
+                        }
+                        if (MORE && !last && (i & 1) && (i >> 1) < LPS && kk * LPS + (i >> 1) < LOADS)
+                            gload(dA, dB, lk0, kk * LPS + (i >> 1));
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
-            }
+            };
+            body(sA + lbuf * STAGE_A, sB + lbuf * STAGE_B, sA + cur * STAGE_A, sB + cur * STAGE_B,
+                 sA + nxt * STAGE_A, sB + nxt * STAGE_B);
         };
         int kt = 0;
         for (; kt + STAGES - 1 < nk; ++kt) kstep(kt, BoolC<true>{}, BoolC<true>{});
@@ -469,8 +563,10 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
                         pk.x = pack2(hv[0], hv[1]);
                         pk.y = pack2(hv[2], hv[3]);
                         *reinterpret_cast<u32x2*>(lt + jl * TSB + il) = pk;
+                        if (dst_d) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) ldr[(il + e) * DSB + jl] = hv[e];
+                            for (int e = 0; e < 4; ++e) ldr[(il + e) * DSB + jl] = hv[e];
+                        }
                     } else if (d.tall) {
                         floatx4 o;
                         o.x = v[0]; o.y = v[1]; o.z = v[2]; o.w = v[3];
@@ -494,12 +590,15 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
                     *reinterpret_cast<u32x4*>(dst_t + (int64_t)(colh + r) * ld_t + row_base + k * 8) = val;
                 }
             }
-            // direct rows: WM rows of HN values (HN / 8 chunks each)
+            // direct rows: WM rows of HN values (HN / 8 chunks each); X'_r only when the
+            // next Gram runs on small tiles
+            if (dst_d) {
 #pragma unroll
-            for (int it = 0; it < WM * HN / 8 / 64; ++it) {
-                const int c = it * 64 + lane, r = c / (HN / 8), k = c % (HN / 8);
-                const u32x4 val = *reinterpret_cast<const u32x4*>(ldr + r * DSB + k * 8);
-                *reinterpret_cast<u32x4*>(dst_d + (int64_t)(row_base + r) * ld_d + colh + k * 8) = val;
+                for (int it = 0; it < WM * HN / 8 / 64; ++it) {
+                    const int c = it * 64 + lane, r = c / (HN / 8), k = c % (HN / 8);
+                    const u32x4 val = *reinterpret_cast<const u32x4*>(ldr + r * DSB + k * 8);
+                    *reinterpret_cast<u32x4*>(dst_d + (int64_t)(row_base + r) * ld_d + colh + k * 8) = val;
+                }
             }
         } else if (d.tall) {
             // O / W is [n, m]: row j holds WM consecutive i of this tile (WM / 4 chunks)

@@ -93,10 +93,10 @@ __global__ __launch_bounds__(256) void k_cast(CastArgs args) {
         u32x2 packed;
         packed.x = pack2(h[0], h[1]);
         packed.y = pack2(h[2], h[3]);
-        *reinterpret_cast<u32x2*>(d.direct + (int64_t)r * d.cols_p + c0) = packed;
+        if (d.direct) *reinterpret_cast<u32x2*>(d.direct + (int64_t)r * d.cols_p + c0) = packed;
     }
     __syncthreads();
-    {
+    if (d.transp) {
         // transposed copy: output row = input column oc, 16 consecutive input rows
         const int oc = tid >> 2, ob = (tid & 3) * 16;
         unsigned w8[8];

@@ -29,7 +29,7 @@ static_assert(kPad % BigCfg::BM == 0 && kPad % BigCfg::BN == 0, "padding must co
 template <int MODE, class Cfg>
 __global__ __launch_bounds__(256, (Cfg::kLdsBytes > 80 * 1024) ? 1 : 2) void k_ns_gemm(NsArgs args) {
     __shared__ __attribute__((aligned(16))) unsigned short smem[Cfg::kLdsBytes / 2];
-    ns_gemm_tile<MODE, Cfg>(args, smem, smem + Cfg::STAGES * Cfg::BM * Cfg::BK);
+    ns_gemm_tile<MODE, Cfg>(args, smem);
 }
 
 template <class Cfg>

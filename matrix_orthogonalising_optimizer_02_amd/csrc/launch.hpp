@@ -12,7 +12,8 @@ namespace muon {
 // One 64x64 tile per block over the padded [rows_p, cols_p] extent of M [rows, cols].
 // `direct` receives bf16(M') in M's orientation ([rows_p, cols_p]); `transp` the
 // transpose ([cols_p, rows_p]). Flat matrices: direct = X_r, transp = X_c; tall
-// matrices: direct = X_c, transp = X_r. Padding is written as zeros.
+// matrices: direct = X_c, transp = X_r. Padding is written as zeros. A null `direct`
+// or `transp` is skipped (X_r is written only for groups whose Gram uses small tiles).
 struct CastDesc {
     const float* m_in;
     const float* g;        // unused when the launch has use_momentum == 0
@@ -48,7 +49,7 @@ struct FrobArgs {
 enum GemmMode : int {
     kModeGram = 0,     // A = s2 * X X^T                  (symmetric tiles)
     kModePoly = 1,     // B = b A + c A A                  (symmetric tiles)
-    kModeApply = 2,    // X' = s1 * (a X + B X)            bf16 X'_r and X'_c
+    kModeApply = 2,    // X' = s1 * (a X + B X)            bf16 X'_c, and X'_r if xr_next
     kModeFinalO = 3,   // O  = s1 * (a X + B X)            fp32, input orientation
     kModeFinalW = 4,   // W <- decay W - upd_coef O        fused Eq. 4 update
 };

@@ -335,6 +335,10 @@ int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_h
     const int ng = int(gp.mats.size());
     const bool eq6 = update_w && hp.scale_mode == MUON_SCALE_RMS;
     const bool monitor = update_w && update_rms != nullptr;
+    // The big-tile Gram reads X_c (transposing LDS reads), so X_r, the row-major copy, is
+    // produced only when this group's Gram runs on small tiles.
+    NsArgs probe{};
+    const bool need_xr = plan_tiles(gp, probe, true) == kTileSmall;
     // cast
     CastArgs ca{};
     ca.n = ng;
@@ -349,8 +353,8 @@ int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_h
         d.m_out = io[k].m_out;
         unsigned short* xr = reinterpret_cast<unsigned short*>(ws + p.xr[0]);
         unsigned short* xc = reinterpret_cast<unsigned short*>(ws + p.xc[0]);
-        d.direct = p.tall ? xc : xr;
-        d.transp = p.tall ? xr : xc;
+        d.direct = p.tall ? xc : (need_xr ? xr : nullptr);
+        d.transp = p.tall ? (need_xr ? xr : nullptr) : xc;
         d.partial = reinterpret_cast<float*>(ws + p.partial);
         d.rows = int32_t(p.rows);
         d.cols = int32_t(p.cols);
@@ -391,7 +395,7 @@ int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_h
             NsDesc& d = na.d[k];
             d.xr = reinterpret_cast<const unsigned short*>(ws + p.xr[cur]);
             d.xc = reinterpret_cast<const unsigned short*>(ws + p.xc[cur]);
-            d.xr_next = reinterpret_cast<unsigned short*>(ws + p.xr[nxt]);
+            d.xr_next = need_xr ? reinterpret_cast<unsigned short*>(ws + p.xr[nxt]) : nullptr;
             d.xc_next = reinterpret_cast<unsigned short*>(ws + p.xc[nxt]);
             d.a = reinterpret_cast<unsigned short*>(ws + p.a);
             d.b = reinterpret_cast<unsigned short*>(ws + p.b);
