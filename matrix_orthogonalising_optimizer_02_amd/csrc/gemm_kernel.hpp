@@ -513,21 +513,63 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
     const float g2 = first_s * first_s;
     float sq = 0.f;  // final modes: this lane's sum of O^2 (padding contributes exact zeros)
 
+    // Operand of the epilogue math of the polynomial and Apply stages (the mirrored half
+    // of A for b A, X for a X), per half: HN rows j of WM values i, 256 bytes each,
+    // brought in through LDS so that every global access is a full 256-byte row segment
+    // (16 lanes per row, 4 rows per 1 KiB DMA load) instead of 32 rows x 8 bytes per
+    // instruction. Chunk c of row r is stored at position c ^ (r & 15). The block sits
+    // over the direct-staging area: it is read into registers before any staging write,
+    // and x_dma waits until earlier LDS reads of the area are done. (The final Apply
+    // keeps direct loads: its wait for the block would also wait for the first half's
+    // W stores.)
+    constexpr bool kDmaX = (MODE == kModePoly || MODE == kModeApply) && Cfg::kDirect && WM == 128 && HN == 64;
+    unsigned short* const xs = sA + __builtin_amdgcn_readfirstlane(wave) * (Cfg::kEpiWave / 2) + HN * TSB;
+    auto x_dma = [&](int hh) {
+        const unsigned short* src = (MODE == kModePoly) ? d.a : d.xc;
+        const int64_t lds = d.m_p;
+        wait_lgkm0();
+        const int lr = lane >> 4, lp = lane & 15;
+        const unsigned short* gsrc = src + (int64_t)(col_base + hh * HN + lr) * lds + row_base;
+#pragma unroll
+        for (int q = 0; q < HN / 4; ++q) {
+            const int r = 4 * q + lr;
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(gsrc + (int64_t)(4 * q) * lds + ((lp ^ (r & 15)) << 3)),
+                                             (lds_ptr_t)(xs + q * 512), 16, 0, 0);
+        }
+    };
+    auto x_read = [&](u32x2 (&ov)[TM][NBH][4]) {
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int bb = 0; bb < NBH; ++bb)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int jl = bb * 32 + lj, ch = a * 4 + rg;
+                    ov[a][bb][rg] = *reinterpret_cast<const u32x2*>(xs + jl * WM + ((ch ^ (jl & 15)) << 3) + li);
+                }
+    };
+
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         // operands of the epilogue math for this half: 8 contiguous bytes per (a, b, rg)
         u32x2 opv[TM][NBH][4];
         if constexpr (MODE != kModeGram) {
-            const unsigned short* src = (MODE == kModePoly) ? d.a : d.xc;
-            const int64_t lds = d.m_p;  // A is [m_p, m_p]; X_c is [n_p, m_p]
+            if constexpr (kDmaX) {
+                x_dma(h);
+                wait_vmcnt<0>();
+                x_read(opv);
+            } else {
+                const unsigned short* src = (MODE == kModePoly) ? d.a : d.xc;
+                const int64_t lds = d.m_p;  // A is [m_p, m_p]; X_c is [n_p, m_p]
 #pragma unroll
-            for (int a = 0; a < TM; ++a)
+                for (int a = 0; a < TM; ++a)
 #pragma unroll
-                for (int bb = 0; bb < NBH; ++bb)
+                    for (int bb = 0; bb < NBH; ++bb)
 #pragma unroll
-                    for (int rg = 0; rg < 4; ++rg)
-                        opv[a][bb][rg] = *reinterpret_cast<const u32x2*>(
-                            src + (int64_t)(col_base + (h * NBH + bb) * 32 + lj) * lds + row_base + a * 32 + rg * 8 + li);
+                        for (int rg = 0; rg < 4; ++rg)
+                            opv[a][bb][rg] = *reinterpret_cast<const u32x2*>(
+                                src + (int64_t)(col_base + (h * NBH + bb) * 32 + lj) * lds + row_base + a * 32 + rg * 8 + li);
+            }
         }
         // values -> LDS
 #pragma unroll
