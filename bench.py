@@ -335,8 +335,13 @@ def main():
         kernels["colnorm_apply"]["algorithmic_gbs"] = round(
             12.0 * elems_tall / (ms["colnorm_apply"] / cnt["colnorm_apply"] * 1e-3) / 1e9, 1)
     if cnt["cast"]:
+        # read M, G; write M and bf16 X_c (and the row-major X_r for groups whose Gram
+        # runs on 128-wide tiles: fewer than 512 symmetric 256-wide tiles)
+        sym_tiles = sum((math.ceil(min(s) / 256)) * (math.ceil(min(s) / 256) + 1) // 2 for s in shapes)
+        cast_b = 14.0 if (len(shapes) <= 16 and sym_tiles >= 512) else 16.0
+        kernels["cast"]["algorithmic_bytes_per_elem"] = cast_b
         kernels["cast"]["algorithmic_gbs"] = round(
-            16.0 * wl.elements / (ms["cast"] / cnt["cast"] * 1e-3) / 1e9, 1)
+            cast_b * wl.elements / (ms["cast"] / cnt["cast"] * 1e-3) / 1e9, 1)
 
     out = {
         "metric": METRIC,
