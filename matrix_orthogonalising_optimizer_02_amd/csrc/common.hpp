@@ -32,6 +32,15 @@ __device__ __forceinline__ unsigned pack2(unsigned short lo, unsigned short hi) 
     return (unsigned)lo | ((unsigned)hi << 16);
 }
 
+// Panel-blocked layout of the Newton-Schulz work matrices X_c, A and B: element (r, c)
+// of a matrix with `cols` columns (rows padded to a multiple of 256, columns to 32)
+// lives in block (r / 256, c / 32), each block 256 x 32 row-major (16 KiB), blocks of a
+// 256-row panel consecutive. A GEMM K step over such a matrix reads one contiguous
+// block per 256-row operand tile instead of 256 strided 64-byte pieces.
+__device__ __forceinline__ int64_t kb_off(int64_t r, int64_t c, int64_t cols) {
+    return ((((r >> 8) * (cols >> 5)) + (c >> 5)) << 13) + ((r & 255) << 5) + (c & 31);
+}
+
 // max(x, eps) that keeps a NaN x (fmaxf would return eps), so NaN norms propagate.
 __device__ __forceinline__ float max_keep_nan(float x, float eps) { return x < eps ? eps : x; }
 

@@ -220,8 +220,22 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
     else if constexpr (MODE == kModeGram) { P = d.xr; Q = d.xr; ld = d.n_p; K = d.n_p; }
     else if constexpr (MODE == kModePoly) { P = d.a; Q = d.a; ld = d.m_p; K = d.m_p; }
     else { P = d.b; Q = d.xc; ld = d.m_p; K = d.m_p; }
-    const unsigned short* Pt = kTr ? P + (int64_t)ti * BM : P + (int64_t)ti * BM * ld;
-    const unsigned short* Qt = kTr ? Q + (int64_t)tj * BN : Q + (int64_t)tj * BN * ld;
+    // X_c, A and B are panel-blocked (kb_off); only the small-tile Gram's X_r is row-major.
+    // K-major tiles (kTr) start at the tile's first column block; the others at the
+    // tile's first row.
+    constexpr bool kBlk = kTr || MODE != kModeGram;
+    const unsigned short* Pt;
+    const unsigned short* Qt;
+    if constexpr (kTr) {
+        Pt = P + ((int64_t)ti * (BM / 32) << 13);
+        Qt = Q + ((int64_t)tj * (BN / 32) << 13);
+    } else if constexpr (kBlk) {
+        Pt = P + kb_off((int64_t)ti * BM, 0, K);
+        Qt = Q + kb_off((int64_t)tj * BN, 0, K);
+    } else {
+        Pt = P + (int64_t)ti * BM * ld;
+        Qt = Q + (int64_t)tj * BN * ld;
+    }
 
     floatx16 acc[TM][TN];
 #pragma unroll
@@ -248,6 +262,7 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         static_assert(KK >= 2 && KK % 2 == 0, "sub-step parity must restart at 0 every K step");
         static_assert(NFR <= NMF && 2 * LPS <= NMF, "issue slots");
         static_assert(!kTr || (Cfg::IA == 4 && Cfg::IB == 4), "K-major tiles: 16 loads of two rows each");
+        static_assert(kBlk && BK == 32 && BM == 256 && BN == 256, "a direct-load tile is one blocked panel, K step one block");
         // the wave index is uniform: keep it scalar so the LDS destinations (M0) are too
         const int swave = __builtin_amdgcn_readfirstlane(wave);
         const int lrow = lane / CPR, lpc = lane % CPR;
@@ -257,10 +272,11 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
             if constexpr (kTr) {  // slot s: rows (s & 3) + 8 (s >> 2) and that + 4
                 const int sl = swave * Cfg::IA + q;
                 const int row = (sl & 3) + 8 * (sl >> 2) + 4 * (lane >> 5);
-                offa[q] = (int64_t)row * ld + ((lane & 31) << 3);
-            } else {
+                const int c = lane & 31;  // 16-byte chunk of the row's 256 columns
+                offa[q] = ((int64_t)(c >> 2) << 13) + row * 32 + ((c & 3) << 3);
+            } else {  // K-contiguous rows of the tile's panel, K step = one 32-column block
                 const int row = (swave * Cfg::IA + q) * RPI + lrow;
-                offa[q] = (int64_t)row * ld + ((lpc ^ ((row >> Cfg::SWS) & (CPR - 1))) << 3);
+                offa[q] = (int64_t)row * BK + ((lpc ^ ((row >> Cfg::SWS) & (CPR - 1))) << 3);
             }
         }
 #pragma unroll
@@ -268,15 +284,18 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
             if constexpr (kTr) {
                 const int sl = swave * Cfg::IB + q;
                 const int row = (sl & 3) + 8 * (sl >> 2) + 4 * (lane >> 5);
-                offb[q] = (int64_t)row * ld + ((lane & 31) << 3);
+                const int c = lane & 31;
+                offb[q] = ((int64_t)(c >> 2) << 13) + row * 32 + ((c & 3) << 3);
             } else {
                 const int row = (swave * Cfg::IB + q) * RPI + lrow;
-                offb[q] = (int64_t)row * ld + ((lpc ^ ((row >> Cfg::SWS) & (CPR - 1))) << 3);
+                offb[q] = (int64_t)row * BK + ((lpc ^ ((row >> Cfg::SWS) & (CPR - 1))) << 3);
             }
         }
         // one 1 KiB load (idx < LOADS) into the stage whose A and B tiles start at dA, dB
         auto gload = [&](unsigned short* dA, unsigned short* dB, int k0, int idx) {
-            const int64_t kofs = kTr ? (int64_t)k0 * ld : (int64_t)k0;
+            // K-major: rows k0 .. k0 + 31 of panel k0 / 256; otherwise block k0 / 32
+            const int64_t kofs = kTr ? ((((int64_t)(k0 >> 8) * (ld >> 5)) << 13) + ((k0 & 255) << 5))
+                                     : ((int64_t)(k0 >> 5) << 13);
             constexpr int SLOT = kTr ? Cfg::kTrSlot : 512;
             if (idx < Cfg::IA)
                 __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Pt + offa[idx] + kofs),
@@ -399,16 +418,25 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         if (kt < nk) kstep(kt, BoolC<false>{}, BoolC<false>{});
         __syncthreads();
     } else {
+        // element (row, k) of the P / Q tile: blocked work matrices or the row-major X_r
+        auto pa = [&](int row, int k) -> const unsigned short* {
+            if constexpr (kBlk) return P + kb_off((int64_t)ti * BM + row, k, K);
+            else return Pt + (int64_t)row * ld + k;
+        };
+        auto qa = [&](int row, int k) -> const unsigned short* {
+            if constexpr (kBlk) return Q + kb_off((int64_t)tj * BN + row, k, K);
+            else return Qt + (int64_t)row * ld + k;
+        };
         u32x4 ra[Cfg::LA], rb[Cfg::LB];
 #pragma unroll
         for (int p = 0; p < Cfg::LA; ++p) {
             const int c = p * NT + tid, row = c / Cfg::CPR, ch = c % Cfg::CPR;
-            ra[p] = *reinterpret_cast<const u32x4*>(Pt + row * ld + ch * 8);
+            ra[p] = *reinterpret_cast<const u32x4*>(pa(row, ch * 8));
         }
 #pragma unroll
         for (int p = 0; p < Cfg::LB; ++p) {
             const int c = p * NT + tid, row = c / Cfg::CPR, ch = c % Cfg::CPR;
-            rb[p] = *reinterpret_cast<const u32x4*>(Qt + row * ld + ch * 8);
+            rb[p] = *reinterpret_cast<const u32x4*>(qa(row, ch * 8));
         }
 #pragma unroll
         for (int p = 0; p < Cfg::LA; ++p) {
@@ -429,12 +457,12 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
 #pragma unroll
                 for (int p = 0; p < Cfg::LA; ++p) {
                     const int c = p * NT + tid, row = c / Cfg::CPR, ch = c % Cfg::CPR;
-                    ra[p] = *reinterpret_cast<const u32x4*>(Pt + row * ld + k0 + ch * 8);
+                    ra[p] = *reinterpret_cast<const u32x4*>(pa(row, k0 + ch * 8));
                 }
 #pragma unroll
                 for (int p = 0; p < Cfg::LB; ++p) {
                     const int c = p * NT + tid, row = c / Cfg::CPR, ch = c % Cfg::CPR;
-                    rb[p] = *reinterpret_cast<const u32x4*>(Qt + row * ld + k0 + ch * 8);
+                    rb[p] = *reinterpret_cast<const u32x4*>(qa(row, k0 + ch * 8));
                 }
             }
             const unsigned short* a_s = sA + cur * STAGE_A;
@@ -529,11 +557,11 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         const int64_t lds = d.m_p;
         wait_lgkm0();
         const int lr = lane >> 4, lp = lane & 15;
-        const unsigned short* gsrc = src + (int64_t)(col_base + hh * HN + lr) * lds + row_base;
+        const int j0 = col_base + hh * HN;
 #pragma unroll
         for (int q = 0; q < HN / 4; ++q) {
             const int r = 4 * q + lr;
-            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(gsrc + (int64_t)(4 * q) * lds + ((lp ^ (r & 15)) << 3)),
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + kb_off(j0 + r, row_base + ((lp ^ (r & 15)) << 3), lds)),
                                              (lds_ptr_t)(xs + q * 512), 16, 0, 0);
         }
     };
@@ -568,7 +596,7 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
 #pragma unroll
                         for (int rg = 0; rg < 4; ++rg)
                             opv[a][bb][rg] = *reinterpret_cast<const u32x2*>(
-                                src + (int64_t)(col_base + (h * NBH + bb) * 32 + lj) * lds + row_base + a * 32 + rg * 8 + li);
+                                src + kb_off(col_base + (h * NBH + bb) * 32 + lj, row_base + a * 32 + rg * 8 + li, lds));
             }
         }
         // values -> LDS
@@ -629,7 +657,7 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
                 for (int it = 0; it < HN * WM / 8 / 64; ++it) {
                     const int c = it * 64 + lane, r = c / (WM / 8), k = c % (WM / 8);
                     const u32x4 val = *reinterpret_cast<const u32x4*>(lt + r * TSB + k * 8);
-                    *reinterpret_cast<u32x4*>(dst_t + (int64_t)(colh + r) * ld_t + row_base + k * 8) = val;
+                    *reinterpret_cast<u32x4*>(dst_t + kb_off(colh + r, row_base + k * 8, ld_t)) = val;
                 }
             }
             // direct rows: WM rows of HN values (HN / 8 chunks each); X'_r only when the
@@ -639,7 +667,10 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
                 for (int it = 0; it < WM * HN / 8 / 64; ++it) {
                     const int c = it * 64 + lane, r = c / (HN / 8), k = c % (HN / 8);
                     const u32x4 val = *reinterpret_cast<const u32x4*>(ldr + r * DSB + k * 8);
-                    *reinterpret_cast<u32x4*>(dst_d + (int64_t)(row_base + r) * ld_d + colh + k * 8) = val;
+                    // A and B are blocked; the Apply's X'_r is row-major
+                    const int64_t o = (MODE == kModeApply) ? (int64_t)(row_base + r) * ld_d + colh + k * 8
+                                                           : kb_off(row_base + r, colh + k * 8, ld_d);
+                    *reinterpret_cast<u32x4*>(dst_d + o) = val;
                 }
             }
         } else if (d.tall) {

@@ -93,7 +93,10 @@ __global__ __launch_bounds__(256) void k_cast(CastArgs args) {
         u32x2 packed;
         packed.x = pack2(h[0], h[1]);
         packed.y = pack2(h[2], h[3]);
-        if (d.direct) *reinterpret_cast<u32x2*>(d.direct + (int64_t)r * d.cols_p + c0) = packed;
+        if (d.direct) {
+            const int64_t o = d.direct_blk ? kb_off(r, c0, d.cols_p) : (int64_t)r * d.cols_p + c0;
+            *reinterpret_cast<u32x2*>(d.direct + o) = packed;
+        }
     }
     __syncthreads();
     if (d.transp) {
@@ -102,7 +105,8 @@ __global__ __launch_bounds__(256) void k_cast(CastArgs args) {
         unsigned w8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) w8[e] = pack2(tile[ob + 2 * e][oc], tile[ob + 2 * e + 1][oc]);
-        unsigned short* dst = d.transp + (int64_t)(tc * 64 + oc) * d.rows_p + tr * 64 + ob;
+        unsigned short* dst = d.transp + (d.transp_blk ? kb_off(tc * 64 + oc, tr * 64 + ob, d.rows_p)
+                                                       : (int64_t)(tc * 64 + oc) * d.rows_p + tr * 64 + ob);
         u32x4 lo, hi;
         lo.x = w8[0]; lo.y = w8[1]; lo.z = w8[2]; lo.w = w8[3];
         hi.x = w8[4]; hi.y = w8[5]; hi.z = w8[6]; hi.w = w8[7];

@@ -14,6 +14,7 @@ namespace muon {
 // transpose ([cols_p, rows_p]). Flat matrices: direct = X_r, transp = X_c; tall
 // matrices: direct = X_c, transp = X_r. Padding is written as zeros. A null `direct`
 // or `transp` is skipped (X_r is written only for groups whose Gram uses small tiles).
+// X_c is panel-blocked (see kb_off), X_r row-major.
 struct CastDesc {
     const float* m_in;
     const float* g;        // unused when the launch has use_momentum == 0
@@ -21,6 +22,8 @@ struct CastDesc {
     unsigned short* direct;
     unsigned short* transp;
     float* partial;        // one float per tile: sum of M'^2 over the tile
+    int32_t direct_blk;    // nonzero: `direct` is panel-blocked (kb_off), else row-major
+    int32_t transp_blk;    // the same for `transp`
     int32_t rows, cols, rows_p, cols_p;
     int32_t tiles_c;       // cols_p / 64
     int32_t tile_begin;    // first tile of this matrix in the launch

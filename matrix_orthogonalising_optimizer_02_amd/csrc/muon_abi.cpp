@@ -355,6 +355,8 @@ int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_h
         unsigned short* xc = reinterpret_cast<unsigned short*>(ws + p.xc[0]);
         d.direct = p.tall ? xc : (need_xr ? xr : nullptr);
         d.transp = p.tall ? (need_xr ? xr : nullptr) : xc;
+        d.direct_blk = p.tall ? 1 : 0;  // X_c is panel-blocked, X_r row-major
+        d.transp_blk = p.tall ? 0 : 1;
         d.partial = reinterpret_cast<float*>(ws + p.partial);
         d.rows = int32_t(p.rows);
         d.cols = int32_t(p.cols);
