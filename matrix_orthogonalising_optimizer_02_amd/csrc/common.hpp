@@ -41,6 +41,15 @@ __device__ __forceinline__ int64_t kb_off(int64_t r, int64_t c, int64_t cols) {
     return ((((r >> 8) * (cols >> 5)) + (c >> 5)) << 13) + ((r & 255) << 5) + (c & 31);
 }
 
+// Streaming fp32 vector access with the non-temporal hint: the bandwidth-bound passes
+// touch each element once, and the hint measurably raises their HBM throughput.
+__device__ __forceinline__ floatx4 ld_stream(const float* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
+}
+__device__ __forceinline__ void st_stream(float* p, floatx4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<floatx4*>(p));
+}
+
 // max(x, eps) that keeps a NaN x (fmaxf would return eps), so NaN norms propagate.
 __device__ __forceinline__ float max_keep_nan(float x, float eps) { return x < eps ? eps : x; }
 

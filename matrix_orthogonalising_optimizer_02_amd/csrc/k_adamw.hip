@@ -36,10 +36,10 @@ __global__ __launch_bounds__(256) void k_adamw(AdamArgs args) {
 #pragma unroll
         for (int k = 0; k < kV; ++k) {
             const int64_t i = base + (int64_t)(k * 256 + threadIdx.x) * 4;
-            wv[k] = *reinterpret_cast<const floatx4*>(d.w + i);
-            gv[k] = *reinterpret_cast<const floatx4*>(d.g + i);
-            mv[k] = *reinterpret_cast<const floatx4*>(d.m + i);
-            vv[k] = *reinterpret_cast<const floatx4*>(d.v + i);
+            wv[k] = ld_stream(d.w + i);
+            gv[k] = ld_stream(d.g + i);
+            mv[k] = ld_stream(d.m + i);
+            vv[k] = ld_stream(d.v + i);
         }
 #pragma unroll
         for (int k = 0; k < kV; ++k) {
@@ -52,9 +52,9 @@ __global__ __launch_bounds__(256) void k_adamw(AdamArgs args) {
                 mv[k][e] = m;
                 vv[k][e] = v;
             }
-            *reinterpret_cast<floatx4*>(d.w + i) = w;
-            *reinterpret_cast<floatx4*>(d.m + i) = mv[k];
-            *reinterpret_cast<floatx4*>(d.v + i) = vv[k];
+            st_stream(d.w + i, w);
+            st_stream(d.m + i, mv[k]);
+            st_stream(d.v + i, vv[k]);
         }
     } else {
         for (int64_t i = base + threadIdx.x; i < d.n; i += 256) {

@@ -44,8 +44,8 @@ __global__ __launch_bounds__(256) void k_cast(CastArgs args) {
             const int r = tr * 64 + rq + 16 * q;
             const bool ok = r < d.rows && c0 + 3 < d.cols;
             const int64_t o = (int64_t)r * d.cols + c0;
-            mm[q] = ok ? *reinterpret_cast<const floatx4*>(d.m_in + o) : floatx4{0.f, 0.f, 0.f, 0.f};
-            gg[q] = (ok && mom) ? *reinterpret_cast<const floatx4*>(d.g + o) : floatx4{0.f, 0.f, 0.f, 0.f};
+            mm[q] = ok ? ld_stream(d.m_in + o) : floatx4{0.f, 0.f, 0.f, 0.f};
+            gg[q] = (ok && mom) ? ld_stream(d.g + o) : floatx4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void k_cast(CastArgs args) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) m[e] = fmaf(mu, m[e], gg[q][e]);
             }
-            if (ok && d.m_out) *reinterpret_cast<floatx4*>(d.m_out + (int64_t)r * d.cols + c0) = m;
+            if (ok && d.m_out) st_stream(d.m_out + (int64_t)r * d.cols + c0, m);
 #pragma unroll
             for (int e = 0; e < 4; ++e) vv[q][e] = m[e];
         }
@@ -166,9 +166,9 @@ __global__ __launch_bounds__(256) void k_rownorm_rows(RowArgs args) {
         // written through a pointer that the compiler cannot prove distinct from G's).
         constexpr int kB = 4;
         floatx4 mv[VMAX];
-        const floatx4* gp = reinterpret_cast<const floatx4*>(d.g + base);
-        floatx4* mp = reinterpret_cast<floatx4*>(d.m + base);
-        floatx4* wp = reinterpret_cast<floatx4*>(d.w + base);
+        const float* gp = d.g + base;
+        float* mp = d.m + base;
+        float* wp = d.w + base;
         const int nv = d.cols >> 2;
 #pragma unroll
         for (int k0 = 0; k0 < VMAX; k0 += kB) {
@@ -177,8 +177,8 @@ __global__ __launch_bounds__(256) void k_rownorm_rows(RowArgs args) {
             for (int k = k0; k < k0 + kB && k < VMAX; ++k) {
                 const int idx = k * 256 + tid;
                 if (idx < nv) {
-                    mv[k] = mp[idx];
-                    gv[k - k0] = gp[idx];
+                    mv[k] = ld_stream(mp + 4 * idx);
+                    gv[k - k0] = ld_stream(gp + 4 * idx);
                 }
             }
 #pragma unroll
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256) void k_rownorm_rows(RowArgs args) {
                         mv[k][e] = fmaf(mu, mv[k][e], gv[k - k0][e]);
                         ss = fmaf(mv[k][e], mv[k][e], ss);
                     }
-                    mp[idx] = mv[k];
+                    st_stream(mp + 4 * idx, mv[k]);
                 }
             }
         }
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256) void k_rownorm_rows(RowArgs args) {
 #pragma unroll
             for (int k = k0; k < k0 + kB && k < VMAX; ++k) {
                 const int idx = k * 256 + tid;
-                if (idx < nv) wv[k - k0] = wp[idx];
+                if (idx < nv) wv[k - k0] = ld_stream(wp + 4 * idx);
             }
 #pragma unroll
             for (int k = k0; k < k0 + kB && k < VMAX; ++k) {
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) void k_rownorm_rows(RowArgs args) {
                     floatx4 w = wv[k - k0];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) w[e] = fmaf(-c, mv[k][e], w[e] * decay);
-                    wp[idx] = w;
+                    st_stream(wp + 4 * idx, w);
                 }
             }
         }
@@ -316,8 +316,8 @@ __global__ __launch_bounds__(256) void k_colnorm_partial(ColArgs args) {
                 const int r = rb + 4 * q;
                 if (r < r1) {
                     const int64_t o = (int64_t)r * d.cols + c0;
-                    mv[q] = *reinterpret_cast<const floatx4*>(d.m + o);
-                    gv[q] = *reinterpret_cast<const floatx4*>(d.g + o);
+                    mv[q] = ld_stream(d.m + o);
+                    gv[q] = ld_stream(d.g + o);
                 }
             }
 #pragma unroll
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(256) void k_colnorm_partial(ColArgs args) {
                     floatx4 m = mv[q];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) m[e] = fmaf(mu, m[e], gv[q][e]);
-                    *reinterpret_cast<floatx4*>(d.m + (int64_t)r * d.cols + c0) = m;
+                    st_stream(d.m + (int64_t)r * d.cols + c0, m);
                     s0 = fmaf(m[0], m[0], s0);
                     s1 = fmaf(m[1], m[1], s1);
                     s2 = fmaf(m[2], m[2], s2);
@@ -400,8 +400,8 @@ __global__ __launch_bounds__(256) void k_colnorm_apply(ColArgs args) {
                 const int r = rb + 4 * q;
                 if (r < r1) {
                     const int64_t o = (int64_t)r * d.cols + c0;
-                    mv[q] = *reinterpret_cast<const floatx4*>(d.m + o);
-                    wv[q] = *reinterpret_cast<const floatx4*>(d.w + o);
+                    mv[q] = ld_stream(d.m + o);
+                    wv[q] = ld_stream(d.w + o);
                 }
             }
 #pragma unroll
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(256) void k_colnorm_apply(ColArgs args) {
                     floatx4 w = wv[q];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) w[e] = fmaf(-kc[e], mv[q][e], w[e] * decay);
-                    *reinterpret_cast<floatx4*>(d.w + (int64_t)r * d.cols + c0) = w;
+                    st_stream(d.w + (int64_t)r * d.cols + c0, w);
                 }
             }
         }
@@ -494,8 +494,8 @@ __global__ __launch_bounds__(256) void k_scaled_update(UpdArgs args) {
 #pragma unroll
         for (int k = 0; k < kV; ++k) {
             const int64_t i = base + (int64_t)(k * 256 + threadIdx.x) * 4;
-            ov[k] = *reinterpret_cast<const floatx4*>(d.o + i);
-            wv[k] = *reinterpret_cast<const floatx4*>(d.w + i);
+            ov[k] = ld_stream(d.o + i);
+            wv[k] = ld_stream(d.w + i);
         }
 #pragma unroll
         for (int k = 0; k < kV; ++k) {
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(256) void k_scaled_update(UpdArgs args) {
             floatx4 w = wv[k];
 #pragma unroll
             for (int e = 0; e < 4; ++e) w[e] = fmaf(-coef, ov[k][e], w[e] * decay);
-            *reinterpret_cast<floatx4*>(d.w + i) = w;
+            st_stream(d.w + i, w);
         }
     } else {
         for (int64_t i = base + threadIdx.x; i < d.elems; i += 256) d.w[i] = fmaf(-coef, d.o[i], d.w[i] * decay);
