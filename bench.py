@@ -92,7 +92,8 @@ def pick_workload(name):
 def cpu_baseline(wl, k):
     """Time the float64 oracle on the workload's smallest matrix and scale to the set.
 
-    Sample: one refresh step and one RowNorm step of the oracle on one matrix.
+    Sample: the median of three refresh steps and of three RowNorm steps of the oracle
+    on one matrix (about 12 s of host work).
     The refresh time is scaled by the oracle's own flop count (Eq. 2 as written:
     X X^T, A X and A (A X), 8 m^2 n per iteration) and the RowNorm time by elements.
     """
@@ -109,12 +110,16 @@ def cpu_baseline(wl, k):
     shape = wl.shapes[idx]
     w, m, g = WL.host_inputs(wl, idx)
     hp = O.OracleHParams(period_k=k)
-    t0 = time.perf_counter()
-    O.vanilla_step(w, m, g, hp)
-    t_ref = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    O.rownorm_step(w, m, g, hp)
-    t_rn = time.perf_counter() - t0
+    reps = 3  # median of three: about 12 s of host work on the 5120 x 5120 matrix
+    t_refs, t_rns = [], []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        O.vanilla_step(w, m, g, hp)
+        t_refs.append(time.perf_counter() - t0)
+        t0 = time.perf_counter()
+        O.rownorm_step(w, m, g, hp)
+        t_rns.append(time.perf_counter() - t0)
+    t_ref, t_rn = sorted(t_refs)[reps // 2], sorted(t_rns)[reps // 2]
 
     def oflops(s):
         mm, nn = min(s), max(s)
@@ -124,9 +129,9 @@ def cpu_baseline(wl, k):
     rn_total = t_rn * wl.elements / (shape[0] * shape[1])
     avg_ms = 1e3 * (ref_total + (k - 1) * rn_total) / k
     return {"value": round(avg_ms, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle refresh step ({t_ref:.1f} s) and RowNorm step ({t_rn:.2f} s) on the "
-                      f"{shape[0]}x{shape[1]} matrix, scaled by flops and elements to the {len(wl.shapes)}-matrix "
-                      f"set; value = mean ms per optimizer step over a K={k} cycle",
+            "sample": f"oracle refresh step ({t_ref:.1f} s) and RowNorm step ({t_rn:.2f} s), medians of "
+                      f"{reps} runs on the {shape[0]}x{shape[1]} matrix, scaled by flops and elements to the "
+                      f"{len(wl.shapes)}-matrix set; value = mean ms per optimizer step over a K={k} cycle",
             "vanilla_step_ms": round(1e3 * ref_total, 1), "rownorm_step_ms": round(1e3 * rn_total, 1)}
 
 
