@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 2
+#define MUON_ABI_VERSION 3
 
 /* Status codes returned by every entry point. */
 #define MUON_OK 0
@@ -105,7 +105,12 @@ typedef struct muon_matrix {
 #define MUON_KCLASS_RMS_FINALIZE 10    /* per-matrix RMS(U): monitor value, Eq. 6 factor */
 #define MUON_KCLASS_SCALED_UPDATE 11   /* Eq. 6 refresh: W <- decay W - coef O */
 #define MUON_KCLASS_ADAMW 12           /* AdamW companion (non-matrix parameters) */
-#define MUON_KCLASS_COUNT 13
+#define MUON_KCLASS_SPEC_GRAM 13       /* SVD entropy: fp64 Gram matrix (fp64 MFMA) */
+#define MUON_KCLASS_SPEC_HOUSE 14      /* SVD entropy: Householder reflector per column */
+#define MUON_KCLASS_SPEC_PASS 15       /* SVD entropy: trailing update + matrix-vector product */
+#define MUON_KCLASS_SPEC_BISECT 16     /* SVD entropy: eigenvalues by Sturm bisection */
+#define MUON_KCLASS_SPEC_ENTROPY 17    /* SVD entropy: normalisation and entropy */
+#define MUON_KCLASS_COUNT 18
 
 /* Returns MUON_ABI_VERSION. Host only. */
 int muon_abi_version(void);
@@ -206,6 +211,37 @@ void adamw_default_hparams(adamw_hparams* hp);
  * w, m, v, g ranges overlap), TOO_LARGE (numel above 2^40), HIP. */
 int adamw_step(const adamw_param* params, int32_t count, const adamw_hparams* hp, int64_t step,
                void* stream);
+
+/* ---- Singular-spectrum diagnostic ----------------------------------------------------
+ * SVD entropy of "Muon is Scalable for LLM Training", Sec. 3.4 (Dynamics of Singular
+ * Spectrum): for W [A, B] with singular values sigma_1..sigma_n, n = min(A, B),
+ *   q_i = sigma_i^2 / sum_j sigma_j^2,   H = -(1 / log n) sum_i q_i log q_i,
+ * 1 for a flat spectrum and 0 for rank one. Zero singular values contribute 0; n = 1
+ * gives 0; an all-zero matrix gives NaN (nothing to normalise).
+ * Computed in fp64 on the device: sigma_i^2 are the eigenvalues of the Gram matrix
+ * X X^T (X = W, or W^T when A > B), reduced to tridiagonal form by Householder
+ * reflections and solved by Sturm-count bisection. The cost is about
+ * 2 min(A,B)^2 max(A,B) fp64 MFMA flops plus 16 min(A,B)^3 / 3 bytes of memory
+ * traffic, so this is an occasional diagnostic, not a per-step call. */
+
+/* Workspace in bytes for svd_entropy on `count` matrices of shapes rows[i] x cols[i]
+ * (about 8 min(A,B)^2 bytes per matrix for up to 16 matrices at a time). Host only.
+ * Errors: INVALID_ARG (NULL bytes, count < 0, NULL rows/cols with count > 0, negative
+ * dims), TOO_LARGE (as muon_workspace_bytes, or min(A, B) above 65536). */
+int svd_entropy_workspace_bytes(const int64_t* rows, const int64_t* cols, int32_t count, size_t* bytes);
+
+/* entropy[i] = H(w[i]) for the fp32 DEVICE matrices w[i] of shape rows[i] x cols[i]
+ * (host arrays of `count` entries; row-major, 16-byte aligned, read only).
+ * entropy: DEVICE array of `count` doubles, 8-byte aligned.
+ * sigma_sq: optional DEVICE array (NULL = not wanted) of sum_i min(rows[i], cols[i])
+ *   doubles, 8-byte aligned; matrix i's sigma^2 in descending order start at
+ *   sum_{k<i} min(rows[k], cols[k]). Eigenvalues below 0 by rounding are reported as 0.
+ * Empty matrices are skipped (their entropy entry is left unchanged). Outputs must not
+ * overlap each other, the inputs or the workspace.
+ * Errors: INVALID_ARG, ALIGN, ALIAS, WORKSPACE, TOO_LARGE, HIP. */
+int svd_entropy(const float* const* w, const int64_t* rows, const int64_t* cols, int32_t count,
+                void* workspace, size_t workspace_bytes, double* entropy, double* sigma_sq,
+                void* stream);
 
 /* Optional per-kernel-class timing. While enabled (enable != 0), every kernel the
  * library enqueues is bracketed by HIP events recorded on the caller's stream.

@@ -21,6 +21,8 @@ from .binding import (  # noqa: F401
     muon_step,
     ns5_batched,
     rownorm_update,
+    svd_entropy,
+    svd_entropy_workspace_bytes,
     timing_enable,
     timing_read,
     workspace_bytes,

@@ -27,11 +27,13 @@ SCALE_RMS = 2       # 0.2 / RMS(O), Eq. 6
 
 KCLASS_NAMES = ("cast", "frob", "gram", "poly", "apply", "apply_final", "rownorm_rows",
                 "colnorm_partial", "colnorm_finalize", "colnorm_apply", "rms_finalize",
-                "scaled_update", "adamw")
+                "scaled_update", "adamw", "spec_gram", "spec_house", "spec_pass", "spec_bisect",
+                "spec_entropy")
 
 EXPORTED = ("muon_abi_version", "muon_status_str", "muon_last_error", "muon_default_hparams",
             "muon_workspace_bytes", "muon_step", "ns5_batched", "rownorm_update",
-            "adamw_default_hparams", "adamw_step", "muon_timing_enable", "muon_timing_read")
+            "adamw_default_hparams", "adamw_step", "svd_entropy_workspace_bytes", "svd_entropy",
+            "muon_timing_enable", "muon_timing_read")
 
 
 class MuonHParams(ctypes.Structure):
@@ -96,10 +98,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.adamw_default_hparams.argtypes = [ctypes.POINTER(AdamWHParams)]
     lib.adamw_default_hparams.restype = None
     lib.adamw_step.argtypes = [ctypes.POINTER(AdamWParam), i32, ctypes.POINTER(AdamWHParams), i64, vp]
+    lib.svd_entropy_workspace_bytes.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                                i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.svd_entropy.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                i32, vp, sz, vp, vp, vp]
     lib.muon_timing_enable.argtypes = [ctypes.c_int]
     lib.muon_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     for name in ("muon_step", "ns5_batched", "rownorm_update", "muon_workspace_bytes", "adamw_step",
-                 "muon_timing_enable", "muon_timing_read"):
+                 "svd_entropy_workspace_bytes", "svd_entropy", "muon_timing_enable", "muon_timing_read"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -321,6 +327,64 @@ def adamw_step(params, grads, exp_avgs, exp_avg_sqs, step: int, hp: Optional[Ada
                stream=None):
     """One AdamW step (0-based `step`) over tensors of any shape, in place."""
     AdamWGroup(params, grads, exp_avgs, exp_avg_sqs, hp).step(step, stream)
+
+
+# ------------------------------------------------------- spectrum diagnostic ----
+
+def _shape_arrays(shapes):
+    n = len(shapes)
+    rows = (ctypes.c_int64 * max(n, 1))(*[int(s[0]) for s in shapes])
+    cols = (ctypes.c_int64 * max(n, 1))(*[int(s[1]) for s in shapes])
+    return rows, cols
+
+
+def svd_entropy_workspace_bytes(shapes: Sequence[Sequence[int]]) -> int:
+    rows, cols = _shape_arrays(shapes)
+    out = ctypes.c_size_t(0)
+    _check(load_library().svd_entropy_workspace_bytes(rows, cols, len(shapes), ctypes.byref(out)),
+           "svd_entropy_workspace_bytes")
+    return int(out.value)
+
+
+def make_svd_entropy_workspace(shapes, device="cuda"):
+    torch = _torch()
+    return torch.empty(max(svd_entropy_workspace_bytes(shapes), 1), dtype=torch.uint8, device=device)
+
+
+def svd_entropy(weights, entropy=None, sigma_sq=None, workspace=None, stream=None):
+    """SVD entropy of each 2-D fp32 device matrix ("Muon is Scalable", Sec. 3.4).
+
+    Returns the float64 device tensor `entropy` [len(weights)] (new when not given).
+    sigma_sq: optional float64 device tensor of sum(min(A, B)) entries that receives
+    every matrix's squared singular values, descending, one matrix after another.
+    """
+    torch = _torch()
+    n = len(weights)
+    dev = weights[0].device if weights else None
+    for i, w in enumerate(weights):
+        _check_tensor(w, f"weights[{i}]")
+    shapes = [tuple(w.shape) for w in weights]
+    if entropy is None:
+        entropy = torch.full((n,), float("nan"), dtype=torch.float64, device=dev)
+    for t, nm, size in ((entropy, "entropy", n), (sigma_sq, "sigma_sq", sum(min(s) for s in shapes))):
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float64 or t.dim() != 1 \
+                or not t.is_contiguous() or t.numel() != size:
+            raise ValueError(f"{nm} must be a contiguous float64 tensor of {size} entries")
+        if size and t.device.type != "cuda":
+            raise ValueError(f"{nm} must live on a GPU")
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[w.data_ptr() or None for w in weights])
+    rows, cols = _shape_arrays(shapes)
+    if workspace is None:
+        workspace = make_svd_entropy_workspace(shapes, dev)
+    rc = load_library().svd_entropy(ptrs, rows, cols, n, ctypes.c_void_p(workspace.data_ptr()),
+                                    ctypes.c_size_t(workspace.numel()),
+                                    ctypes.c_void_p(entropy.data_ptr() or None),
+                                    ctypes.c_void_p(sigma_sq.data_ptr() if sigma_sq is not None else None),
+                                    _stream_handle(stream, dev))
+    _check(rc, "svd_entropy")
+    return entropy
 
 
 def timing_enable(enable: bool = True):

@@ -190,6 +190,46 @@ struct AdamArgs {
     float inv_sqrt_bc2;    // 1 / sqrt(1 - beta2^t)
 };
 
+// ---- singular-spectrum diagnostic (SVD entropy), fp64 throughout -------------------
+// For X = W (rows <= cols) or W^T (rows > cols), [m, n], the eigenvalues of the Gram
+// matrix S = X X^T are sigma_i^2. S (m_p x m_p, m_p = m rounded up to kSpTile, zero
+// padding) is reduced to tridiagonal form by Householder reflections, one column per
+// step: step j's house kernel forms reflector v_j from column j (after the previous
+// step's rank-2 update, applied on the fly) and the pass kernel applies that update
+// to the trailing block while computing p_j = tau_j S v_j in the same sweep. The
+// eigenvalues of the tridiagonal matrix come from Sturm-count bisection.
+constexpr int kSpTile = 128;        // Gram block tile (4 waves of 64 x 64)
+constexpr int kSpRowsPerBlock = 16; // pass kernel: 4 waves x 4 rows
+constexpr int kSpBisectIters = 80;  // bound on bisection halvings (stops earlier)
+
+struct SpDesc {
+    const float* w;        // [rows, cols] fp32 row-major input
+    int64_t cols;          // leading dimension of w
+    int32_t m, n;          // working dims: m = min(rows, cols), n = max
+    int32_t tall;          // rows > cols: X = W^T
+    int32_t tm;            // Gram tiles per side, ceil(m / kSpTile)
+    int32_t tile_begin;    // first Gram tile of this matrix in the launch
+    int32_t sigma_off;     // offset of this matrix's values in sigma_sq (if any)
+    int64_t ld;            // leading dimension of s (m_p)
+    double* s;             // symmetric work matrix, m_p x m_p
+    double* v[2];          // Householder vectors v_j in v[j & 1] (entries j+1 .. m-1)
+    double* wv;            // w_{j-1} = p_{j-1} - (tau_{j-1} / 2) (p_{j-1} . v_{j-1}) v_{j-1}
+    double* p;             // p_j = tau_j S^(j) v_j
+    double* d;             // tridiagonal: diagonal (m)
+    double* e;             // tridiagonal: sub-diagonal (m - 1)
+    double* lam;           // eigenvalues, ascending (m)
+    double* tau;           // tau_j in tau[j & 1]
+    double* entropy;       // output: one value
+};
+
+struct SpArgs {
+    SpDesc d[kMaxGroup];
+    int32_t n;
+    int32_t total;         // Gram: total tiles of the launch
+    int32_t j;             // house / pass: the column step
+    double* sigma_sq;      // optional output, descending per matrix (null = not wanted)
+};
+
 constexpr int kColChunkRows = 256;
 constexpr int kColTileCols = 256;
 // Rows up to this length keep M' in registers (one 256-thread block per row).
@@ -207,6 +247,11 @@ hipError_t launch_colnorm_apply(const ColArgs& a, bool vec, hipStream_t s);
 hipError_t launch_rms_finalize(const RmsArgs& a, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs& a, hipStream_t s);
 hipError_t launch_scaled_update(const UpdArgs& a, hipStream_t s);
+hipError_t launch_sp_gram(const SpArgs& a, hipStream_t s);
+hipError_t launch_sp_house(const SpArgs& a, hipStream_t s);
+hipError_t launch_sp_pass(const SpArgs& a, int max_trailing, hipStream_t s);
+hipError_t launch_sp_bisect(const SpArgs& a, int max_m, hipStream_t s);
+hipError_t launch_sp_entropy(const SpArgs& a, hipStream_t s);
 
 // GEMM block tiles (host-side tile counting must match the kernels).
 #ifndef MUON_GEMM_BIG_M

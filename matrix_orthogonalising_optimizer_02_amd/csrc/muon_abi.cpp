@@ -582,6 +582,120 @@ int do_rownorm(const muon_matrix* mats, int32_t count, const muon_hparams* hp, v
     return MUON_OK;
 }
 
+// ------------------------------------------------------ singular spectrum ----
+// SVD-entropy diagnostic ("Muon is Scalable", Sec. 3.4). Per matrix: the fp64 Gram
+// matrix S (m_p x m_p), seven m_p vectors (v_j twice, w, p, d, e, eigenvalues) and
+// tau; groups of up to kMaxGroup matrices (largest m first) share one workspace
+// region and run one after another.
+constexpr int64_t kSpMaxM = 65536;
+
+struct SpMat {
+    int idx;
+    int64_t rows, cols;
+    int32_t m, n, tm;
+    bool tall;
+    int64_t m_p;
+    size_t off;          // workspace offset relative to the group base
+    int64_t sigma_off;   // offset into the caller's sigma_sq array
+};
+
+struct SpPlan {
+    std::vector<std::vector<SpMat>> groups;
+    size_t bytes = 0;
+    int64_t sigma_total = 0;
+};
+
+size_t sp_vec_bytes(int64_t m_p) { return align256(size_t(m_p) * 8); }
+size_t sp_mat_bytes(int64_t m_p) { return align256(size_t(m_p) * size_t(m_p) * 8) + 7 * sp_vec_bytes(m_p) + 256; }
+
+int make_sp_plan(const int64_t* rows, const int64_t* cols, int32_t count, SpPlan* plan) {
+    if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count < 0");
+    if (count > 0 && (!rows || !cols)) return fail(MUON_ERR_INVALID_ARG, "rows or cols is NULL");
+    std::vector<SpMat> mats;
+    for (int i = 0; i < count; ++i) {
+        const int64_t r = rows[i], c = cols[i];
+        if (r < 0 || c < 0) return fail(MUON_ERR_INVALID_ARG, "negative dimension at index " + std::to_string(i));
+        if (r == 0 || c == 0) continue;
+        if (r > kMaxDim || c > kMaxDim || r * c > kMaxElems)
+            return fail(MUON_ERR_TOO_LARGE, "matrix " + std::to_string(i) + " too large");
+        if (std::min(r, c) > kSpMaxM)
+            return fail(MUON_ERR_TOO_LARGE, "matrix " + std::to_string(i) + ": min(rows, cols) above 65536");
+        SpMat sm{};
+        sm.idx = i;
+        sm.rows = r;
+        sm.cols = c;
+        sm.tall = r > c;
+        sm.m = int32_t(std::min(r, c));
+        sm.n = int32_t(std::max(r, c));
+        sm.m_p = round_up(sm.m, kSpTile);
+        sm.tm = int32_t(sm.m_p / kSpTile);
+        sm.sigma_off = plan->sigma_total;
+        plan->sigma_total += sm.m;
+        mats.push_back(sm);
+    }
+    std::stable_sort(mats.begin(), mats.end(), [](const SpMat& a, const SpMat& b) { return a.m > b.m; });
+    for (size_t k = 0; k < mats.size(); k += kMaxGroup) {
+        std::vector<SpMat> g(mats.begin() + k, mats.begin() + std::min(mats.size(), k + kMaxGroup));
+        size_t off = 0;
+        for (SpMat& sm : g) {
+            sm.off = off;
+            off += sp_mat_bytes(sm.m_p);
+        }
+        plan->bytes = std::max(plan->bytes, off);
+        plan->groups.push_back(std::move(g));
+    }
+    return MUON_OK;
+}
+
+int run_spectrum(const std::vector<SpMat>& g, const float* const* w, char* ws, double* entropy,
+                 double* sigma_sq, hipStream_t s) {
+    SpArgs a{};
+    a.n = int32_t(g.size());
+    a.sigma_sq = sigma_sq;
+    int32_t tiles = 0, max_m = 0;
+    for (int k = 0; k < a.n; ++k) {
+        const SpMat& sm = g[k];
+        SpDesc& d = a.d[k];
+        d.w = w[sm.idx];
+        d.cols = sm.cols;
+        d.m = sm.m;
+        d.n = sm.n;
+        d.tall = sm.tall ? 1 : 0;
+        d.tm = sm.tm;
+        d.tile_begin = tiles;
+        d.sigma_off = int32_t(sm.sigma_off);
+        d.ld = sm.m_p;
+        char* base = ws + sm.off;
+        d.s = reinterpret_cast<double*>(base);
+        base += align256(size_t(sm.m_p) * size_t(sm.m_p) * 8);
+        double** vecs[7] = {&d.v[0], &d.v[1], &d.wv, &d.p, &d.d, &d.e, &d.lam};
+        for (double** v : vecs) {
+            *v = reinterpret_cast<double*>(base);
+            base += sp_vec_bytes(sm.m_p);
+        }
+        d.tau = reinterpret_cast<double*>(base);
+        d.entropy = entropy + sm.idx;
+        tiles += sm.tm * (sm.tm + 1) / 2;
+        max_m = std::max(max_m, sm.m);
+    }
+    a.total = tiles;
+    int rc = run_kernel(MUON_KCLASS_SPEC_GRAM, s, "spectrum gram", [&] { return launch_sp_gram(a, s); });
+    if (rc) return rc;
+    for (int j = 0; j < max_m; ++j) {
+        a.j = j;
+        rc = run_kernel(MUON_KCLASS_SPEC_HOUSE, s, "spectrum house", [&] { return launch_sp_house(a, s); });
+        if (rc) return rc;
+        if (j <= max_m - 2) {
+            rc = run_kernel(MUON_KCLASS_SPEC_PASS, s, "spectrum pass",
+                            [&] { return launch_sp_pass(a, max_m - j - 1, s); });
+            if (rc) return rc;
+        }
+    }
+    rc = run_kernel(MUON_KCLASS_SPEC_BISECT, s, "spectrum bisect", [&] { return launch_sp_bisect(a, max_m, s); });
+    if (rc) return rc;
+    return run_kernel(MUON_KCLASS_SPEC_ENTROPY, s, "spectrum entropy", [&] { return launch_sp_entropy(a, s); });
+}
+
 }  // namespace
 }  // namespace muon
 
@@ -795,6 +909,61 @@ MUON_API int adamw_step(const adamw_param* params, int32_t count, const adamw_hp
         blocks += nb;
     }
     return flush();
+}
+
+MUON_API int svd_entropy_workspace_bytes(const int64_t* rows, const int64_t* cols, int32_t count,
+                                         size_t* bytes) {
+    g_last_error.clear();
+    if (!bytes) return fail(MUON_ERR_INVALID_ARG, "bytes is NULL");
+    SpPlan plan;
+    const int rc = make_sp_plan(rows, cols, count, &plan);
+    if (rc) return rc;
+    *bytes = plan.bytes;
+    return MUON_OK;
+}
+
+MUON_API int svd_entropy(const float* const* w, const int64_t* rows, const int64_t* cols, int32_t count,
+                         void* workspace, size_t workspace_bytes, double* entropy, double* sigma_sq,
+                         void* stream) {
+    g_last_error.clear();
+    SpPlan plan;
+    int rc = make_sp_plan(rows, cols, count, &plan);
+    if (rc) return rc;
+    if (plan.groups.empty()) return MUON_OK;
+    if (!w) return fail(MUON_ERR_INVALID_ARG, "w is NULL");
+    if (!entropy) return fail(MUON_ERR_INVALID_ARG, "entropy is NULL");
+    if (reinterpret_cast<uintptr_t>(entropy) & 7) return fail(MUON_ERR_ALIGN, "entropy not 8-byte aligned");
+    if (sigma_sq && (reinterpret_cast<uintptr_t>(sigma_sq) & 7))
+        return fail(MUON_ERR_ALIGN, "sigma_sq not 8-byte aligned");
+    std::vector<Range> ranges;
+    for (const auto& g : plan.groups)
+        for (const SpMat& sm : g) {
+            const float* p = w[sm.idx];
+            if (!p) return fail(MUON_ERR_INVALID_ARG, "NULL matrix at index " + std::to_string(sm.idx));
+            if (!aligned16(p)) return fail(MUON_ERR_ALIGN, "matrix not 16-byte aligned at index " + std::to_string(sm.idx));
+            const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+            ranges.push_back({lo, lo + uintptr_t(sm.rows * sm.cols) * 4, false});
+        }
+    const uintptr_t elo = reinterpret_cast<uintptr_t>(entropy);
+    ranges.push_back({elo, elo + uintptr_t(count) * 8, true});
+    if (sigma_sq) {
+        const uintptr_t slo = reinterpret_cast<uintptr_t>(sigma_sq);
+        ranges.push_back({slo, slo + uintptr_t(plan.sigma_total) * 8, true});
+    }
+    if (!workspace) return fail(MUON_ERR_WORKSPACE, "workspace is NULL");
+    if (workspace_bytes < plan.bytes)
+        return fail(MUON_ERR_WORKSPACE, "workspace too small: need " + std::to_string(plan.bytes) + " bytes");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(MUON_ERR_ALIGN, "workspace not 256-byte aligned");
+    const uintptr_t wlo = reinterpret_cast<uintptr_t>(workspace);
+    ranges.push_back({wlo, wlo + plan.bytes, true});
+    rc = check_overlaps(ranges);
+    if (rc) return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    for (const auto& g : plan.groups) {
+        rc = run_spectrum(g, w, static_cast<char*>(workspace), entropy, sigma_sq, s);
+        if (rc) return rc;
+    }
+    return MUON_OK;
 }
 
 MUON_API int muon_timing_enable(int enable) {

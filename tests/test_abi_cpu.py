@@ -52,7 +52,7 @@ def test_header_declares_expected_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.muon_abi_version() == 2
+    assert lib.muon_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -287,3 +287,57 @@ def test_adamw_argument_errors(lib):
     other = (1000, BASE + 4 * span, BASE + 5 * span, BASE + 2 * span, BASE + 6 * span)
     assert call(adam_params([ok, other]), 2) == B.MUON_ERR_ALIAS
     assert lib.muon_last_error().decode() != ""
+
+
+# ------------------------------------------------------- spectrum diagnostic ----
+
+def test_svd_entropy_workspace_planning(lib):
+    assert B.svd_entropy_workspace_bytes([]) == 0
+    assert B.svd_entropy_workspace_bytes([(0, 5), (7, 0)]) == 0
+    one = B.svd_entropy_workspace_bytes([(100, 300)])
+    assert one >= 128 * 128 * 8 + 7 * 128 * 8  # fp64 Gram padded to 128, seven vectors
+    assert B.svd_entropy_workspace_bytes([(300, 100)]) == one  # orientation-free
+    big = B.svd_entropy_workspace_bytes([(5120, 30720)] * 10)
+    assert 10 * 5120 * 5120 * 8 <= big < 10 * 5120 * 5120 * 8 + (1 << 22)
+    many = B.svd_entropy_workspace_bytes([(256, 512)] * 20)  # two groups, region reused
+    assert many == B.svd_entropy_workspace_bytes([(256, 512)] * 16)
+    with pytest.raises(B.MuonError) as e:
+        B.svd_entropy_workspace_bytes([(65537, 70000)])
+    assert e.value.status == B.MUON_ERR_TOO_LARGE
+    with pytest.raises(B.MuonError) as e:
+        B.svd_entropy_workspace_bytes([(-3, 4)])
+    assert e.value.status == B.MUON_ERR_INVALID_ARG
+
+
+def call_entropy(lib, shapes, w_ptrs=None, entropy=BASE * 5, sigma=None, ws=BASE * 4, ws_bytes=1 << 34):
+    n = len(shapes)
+    rows = (ctypes.c_int64 * max(n, 1))(*[s[0] for s in shapes])
+    cols = (ctypes.c_int64 * max(n, 1))(*[s[1] for s in shapes])
+    if w_ptrs is None:
+        w_ptrs = [BASE + (1 << 32) * i for i in range(n)]
+    ptrs = (ctypes.c_void_p * max(n, 1))(*w_ptrs)
+    return lib.svd_entropy(ptrs, rows, cols, n, ctypes.c_void_p(ws) if ws else None, ws_bytes,
+                           ctypes.c_void_p(entropy) if entropy else None,
+                           ctypes.c_void_p(sigma) if sigma else None, None)
+
+
+@fake_only
+def test_svd_entropy_validation(lib):
+    assert call_entropy(lib, []) == B.MUON_OK
+    assert call_entropy(lib, [(0, 8), (9, 0)], w_ptrs=[None, None], entropy=None) == B.MUON_OK
+    assert call_entropy(lib, [(64, 64)], w_ptrs=[None]) == B.MUON_ERR_INVALID_ARG
+    assert call_entropy(lib, [(64, 64)], entropy=None) == B.MUON_ERR_INVALID_ARG
+    assert call_entropy(lib, [(64, 64)], entropy=BASE * 5 + 4) == B.MUON_ERR_ALIGN
+    assert call_entropy(lib, [(64, 64)], sigma=BASE * 6 + 2) == B.MUON_ERR_ALIGN
+    assert call_entropy(lib, [(64, 64)], w_ptrs=[BASE + 8]) == B.MUON_ERR_ALIGN
+    assert call_entropy(lib, [(64, 64)], ws=None) == B.MUON_ERR_WORKSPACE
+    assert call_entropy(lib, [(64, 64)], ws_bytes=1024) == B.MUON_ERR_WORKSPACE
+    assert call_entropy(lib, [(64, 64)], ws=BASE * 4 + 128) == B.MUON_ERR_ALIGN
+    assert call_entropy(lib, [(64, 64)], entropy=BASE + 64) == B.MUON_ERR_ALIAS  # inside W
+    assert call_entropy(lib, [(64, 64), (32, 16)], sigma=BASE * 5 + 8) == B.MUON_ERR_ALIAS  # overlaps entropy
+    assert call_entropy(lib, [(64, 64)], entropy=BASE * 4 + 4096) == B.MUON_ERR_ALIAS  # inside the workspace
+    assert call_entropy(lib, [(70000, 70000)]) == B.MUON_ERR_TOO_LARGE
+    assert call_entropy(lib, [(-1, 5)]) == B.MUON_ERR_INVALID_ARG
+    rows = (ctypes.c_int64 * 1)(4)
+    assert lib.svd_entropy(None, rows, rows, 1, None, 0, None, None, None) == B.MUON_ERR_INVALID_ARG
+    assert lib.svd_entropy(None, None, None, -1, None, 0, None, None, None) == B.MUON_ERR_INVALID_ARG

@@ -1,0 +1,175 @@
+"""GPU parity of the SVD-entropy diagnostic ("Muon is Scalable for LLM Training", Sec. 3.4)
+through the C ABI, against the float64 oracle (library SVD).
+
+The device path is fp64 end to end: an fp64-MFMA Gram matrix of the fp32 weights
+(products of fp32 values are exact in fp64), Householder tridiagonalisation and
+Sturm bisection, all backward stable. By Weyl's inequality each eigenvalue moves by
+at most the norm of the backward error, a small multiple of m u ||S|| (u = 2^-53);
+at m <= 1024 that bounds the error of sigma^2 by 1e-10 of the largest one, with room
+for the worst case, and the entropy, whose sensitivity to one eigenvalue is
+|log q + 1| / (total log m), by 1e-10 as well. At the full 5120 size both bounds are
+taken 10x looser.
+
+Cases: flat, tall and square shapes with ragged tails around the 128 Gram tile and
+the 16-wide K slice; a flat spectrum (entropy 1), rank one (entropy 0), two-level
+and power-law spectra, a zero matrix (NaN), a single singular value (0), more matrices
+than one launch group, empty matrices, determinism, and the full-size 5120 x 5120
+matrix of the 15B-scale layer set together with the other nine in the launch the
+benchmark times.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import spectrum_oracle as S
+from matrix_orthogonalising_optimizer_02_amd import binding as B
+from matrix_orthogonalising_optimizer_02_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+H_TOL = 1e-10
+LAM_TOL = 1e-10
+H_TOL_FULL = 1e-9
+LAM_TOL_FULL = 1e-9
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "the gpu tests need a visible GPU"
+    B.load_library()
+    return torch, torch.device("cuda:0")
+
+
+def orthonormal(rows, cols, rng):
+    q, r = np.linalg.qr(rng.normal(size=(rows, cols)))
+    return q * np.sign(np.diag(r))
+
+
+def with_spectrum(a, b, sigma, seed):
+    rng = np.random.default_rng(seed)
+    n = min(a, b)
+    return (orthonormal(a, n, rng) @ np.diag(sigma) @ orthonormal(b, n, rng).T).astype(np.float32)
+
+
+def run(torch, dev, mats, want_sigma=True):
+    ws = [torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev) for x in mats]
+    sig = None
+    if want_sigma:
+        sig = torch.full((sum(min(x.shape) for x in mats),), -1.0, dtype=torch.float64, device=dev)
+    ent = B.svd_entropy(ws, sigma_sq=sig)
+    torch.cuda.synchronize()
+    return ent.cpu().numpy(), (sig.cpu().numpy() if sig is not None else None)
+
+
+def check(mats, ent, sig, h_tol=H_TOL, lam_tol=LAM_TOL, label=""):
+    off = 0
+    worst_h = worst_l = 0.0
+    for i, x in enumerate(mats):
+        n = min(x.shape)
+        if n == 0:
+            continue
+        xd = np.asarray(x, dtype=np.float64)
+        lam_ref = S.singular_values_sq(xd)
+        h_ref = S.entropy_of_spectrum(lam_ref)
+        if math.isnan(h_ref):
+            assert math.isnan(ent[i]), (label, i, x.shape, ent[i])
+        else:
+            dh = abs(ent[i] - h_ref)
+            worst_h = max(worst_h, dh)
+            assert dh < h_tol, (label, i, x.shape, ent[i], h_ref)
+        if sig is not None:
+            got = sig[off:off + n]
+            scale = lam_ref[0] if lam_ref[0] > 0 else 1.0
+            dl = float(np.max(np.abs(got - lam_ref))) / scale
+            worst_l = max(worst_l, dl)
+            assert dl < lam_tol, (label, i, x.shape, dl)
+            assert np.all(np.diff(got) <= 0.0), (label, i, "not descending")
+        off += n
+    log(f"{label}: {len(mats)} matrices, worst |dH| {worst_h:.2e}, worst sigma^2 err / max {worst_l:.2e}")
+
+
+def test_ragged_flat_tall_square_gaussian(torch_dev):
+    torch, dev = torch_dev
+    shapes = [(1, 7), (2, 2), (3, 50), (50, 3), (127, 300), (129, 129), (200, 130), (257, 1000),
+              (1000, 257), (384, 384), (130, 17), (17, 130)]
+    mats = [WL.host_normal(600, WL.ROLE_W, i, s, 0.02) for i, s in enumerate(shapes)]
+    ent, sig = run(torch, dev, mats)
+    check(mats, ent, sig, label="gaussian")
+
+
+def test_structured_spectra(torch_dev):
+    torch, dev = torch_dev
+    rng = np.random.default_rng(601)
+    flat = (0.5 * orthonormal(300, 140, rng).T).astype(np.float32)          # [140, 300], sigma all 0.5
+    rank1 = np.outer(rng.normal(size=160), rng.normal(size=90)).astype(np.float32)
+    two = with_spectrum(96, 200, [3.0] * 10 + [1.0] * 86, 602)
+    power = with_spectrum(400, 250, [1.0 / (i + 1) for i in range(250)], 603)
+    zero = np.zeros((64, 80), np.float32)
+    single = rng.normal(size=(1, 333)).astype(np.float32)
+    dup = np.repeat(rng.normal(size=(20, 150)), 3, axis=0).astype(np.float32)  # rank 20 of 60
+    big = (1e3 * rng.normal(size=(70, 90))).astype(np.float32)
+    mats = [flat, rank1, two, power, zero, single, dup, big]
+    ent, sig = run(torch, dev, mats)
+    check(mats, ent, sig, label="structured")
+    assert abs(ent[0] - 1.0) < H_TOL and abs(ent[1]) < H_TOL
+    t = 10 * 9.0 + 86 * 1.0
+    h_two = (math.log(t) - 10 * 9.0 * math.log(9.0) / t) / math.log(96)
+    assert abs(ent[2] - h_two) < H_TOL
+    assert math.isnan(ent[4]) and ent[5] == 0.0
+
+
+def test_more_matrices_than_one_group_and_empty_ones(torch_dev):
+    torch, dev = torch_dev
+    shapes = [(40 + 23 * i, 300 - 11 * i) if i % 3 else (260 - 9 * i, 50 + 7 * i) for i in range(19)]
+    shapes[4] = (0, 12)
+    shapes[11] = (33, 0)
+    mats = [WL.host_normal(604, WL.ROLE_W, i, s, 0.02) for i, s in enumerate(shapes)]
+    ent, sig = run(torch, dev, mats)
+    check(mats, ent, sig, label="19 matrices, 2 empty")
+    assert math.isnan(ent[4]) and math.isnan(ent[11])  # skipped: the pre-filled NaN stays
+
+
+def test_scale_invariance_and_determinism(torch_dev):
+    torch, dev = torch_dev
+    x = WL.host_normal(605, WL.ROLE_W, 0, (300, 700), 0.02)
+    ent, _ = run(torch, dev, [x, (x * 64.0).astype(np.float32), np.ascontiguousarray(x.T)], want_sigma=False)
+    assert abs(ent[0] - ent[1]) < 1e-12 and abs(ent[0] - ent[2]) < 1e-12
+    again, _ = run(torch, dev, [x, (x * 64.0).astype(np.float32), np.ascontiguousarray(x.T)], want_sigma=False)
+    assert np.array_equal(ent, again)
+
+
+def test_full_size_layer_set(torch_dev):
+    """The 15B-scale layer set (ten matrices, m = 5120) in one call, as the benchmark
+    times it: the 5120 x 5120 matrix against the oracle's SVD, and for every matrix
+    sum sigma^2 = ||W||_F^2, descending order and 0 < H < 1."""
+    torch, dev = torch_dev
+    wl = WL.LAYER_SET_15B_H5120
+    ws = [torch.empty(s, dtype=torch.float32, device=dev) for s in wl.shapes]
+    for i, t in enumerate(ws):
+        WL.device_fill(t, wl.key, WL.ROLE_W, i, wl.w_std)
+    sig = torch.empty(sum(min(s) for s in wl.shapes), dtype=torch.float64, device=dev)
+    log("full-size svd_entropy: 10 matrices, m = 5120")
+    ent = B.svd_entropy(ws, sigma_sq=sig)
+    torch.cuda.synchronize()
+    ent, sig = ent.cpu().numpy(), sig.cpu().numpy()
+    off = 0
+    for i, (s, t) in enumerate(zip(wl.shapes, ws)):
+        n = min(s)
+        x = t.cpu().numpy().astype(np.float64)
+        fro2 = float(np.sum(x * x))
+        lam = sig[off:off + n]
+        assert abs(lam.sum() - fro2) < 1e-11 * fro2, (i, s)
+        assert np.all(np.diff(lam) <= 0.0) and 0.0 < ent[i] < 1.0, (i, s)
+        if s == (5120, 5120):
+            log("oracle SVD of the 5120 x 5120 matrix")
+            check([x.astype(np.float32)], ent[i:i + 1], lam, H_TOL_FULL, LAM_TOL_FULL, label="full 5120^2")
+        off += n
+    log(f"full-size entropies: {np.round(ent, 6).tolist()}")
