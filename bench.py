@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 METRIC = "Muon step ms per DiT block set; NS5 MFMA TFLOP/s; RowNorm HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP64_TFLOPS = 78.6     # MI355X dense fp64 MFMA
 
 
 def ns5_flops_sym(m, n, steps=5):
@@ -78,6 +79,8 @@ def parse():
                     help="timed steps per scale-rule / monitor variant (0: skip)")
     ap.add_argument("--adamw-steps", type=int, default=5,
                     help="timed AdamW steps over the model's AdamW group (0: skip)")
+    ap.add_argument("--spectrum-calls", type=int, default=1,
+                    help="timed SVD-entropy diagnostic calls over the layer set (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
@@ -224,6 +227,52 @@ def measure_adamw(pkg, torch, dev, wl, n, say):
     return res
 
 
+def measure_spectrum(pkg, torch, weights, n, say):
+    """The SVD-entropy diagnostic over the layer set's weights, fp64 on the device.
+
+    Algorithmic work per matrix (m = min, n = max): the Gram kernel's m (m + 1) n
+    flops (upper triangle with the diagonal, 2 flops per product term), and per
+    Householder column step j the upper triangle of the trailing block (l = m - j - 1
+    rows, l (l + 1) / 2 elements) read and written once, 16 bytes per element (the
+    first step only reads: no pending update).
+    """
+    shapes = [tuple(w.shape) for w in weights]
+    ws = pkg.binding.make_svd_entropy_workspace(shapes, weights[0].device)
+    ent = torch.empty(len(weights), dtype=torch.float64, device=weights[0].device)
+    pkg.svd_entropy(weights, entropy=ent, workspace=ws)  # warm-up
+    torch.cuda.synchronize()
+    pkg.timing_enable(True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        pkg.svd_entropy(weights, entropy=ent, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    kern = pkg.timing_read()
+    pkg.timing_enable(False)
+    call_ms = a.elapsed_time(b) / n
+    gram_flops = sum(float(min(s)) * (min(s) + 1) * max(s) for s in shapes)
+    pass_bytes = sum(16.0 * (min(s) - 1) * min(s) * (min(s) + 1) / 6.0 - 8.0 * (min(s) - 1) * min(s) / 2.0
+                     for s in shapes)
+    per = {nm: kern["spec_" + nm] for nm in ("gram", "house", "pass", "reduce", "bisect", "entropy")}
+    gram_ms = per["gram"][0] / n
+    pass_ms = per["pass"][0] / n
+    res = {"call_ms": round(call_ms, 3),
+           "entropy": [round(float(x), 6) for x in ent.cpu().tolist()],
+           "launches_per_call": sum(c for _, c in per.values()) // n,
+           "kernel_ms_per_call": {nm: round(v[0] / n, 3) for nm, v in per.items()},
+           "gram": {"bound": "mfma", "dtype": "f64", "achieved": round(gram_flops / (gram_ms * 1e-3) / 1e12, 2),
+                    "peak": PEAK_FP64_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(gram_flops / (gram_ms * 1e-3) / 1e12 / PEAK_FP64_TFLOPS, 4)},
+           "householder_pass": {"bound": "hbm", "achieved": round(pass_bytes / (pass_ms * 1e-3) / 1e9, 1),
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(pass_bytes / (pass_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                "avg_launch_ms": round(per["pass"][0] / max(per["pass"][1], 1), 4)}}
+    say(f"spectrum: {res}")
+    del ws
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -305,6 +354,7 @@ def main():
     variants = measure_variants(pkg, torch, weights, momenta, grads, ws, k, wl, args.variant_steps, say) \
         if args.variant_steps > 0 else None
     hybrid = measure_adamw(pkg, torch, dev, wl, args.adamw_steps, say) if args.adamw_steps > 0 else None
+    spectrum = measure_spectrum(pkg, torch, weights, args.spectrum_calls, say) if args.spectrum_calls > 0 else None
 
     refreshes = args.steps
     rownorm_steps = args.steps * (k - 1)
@@ -384,6 +434,8 @@ def main():
         out["variants"] = variants
     if hybrid is not None:
         out["hybrid"] = hybrid
+    if spectrum is not None:
+        out["spectrum"] = spectrum
     if not args.no_cpu_baseline:
         say("cpu baseline: timing the float64 oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(wl, k)

@@ -107,10 +107,11 @@ typedef struct muon_matrix {
 #define MUON_KCLASS_ADAMW 12           /* AdamW companion (non-matrix parameters) */
 #define MUON_KCLASS_SPEC_GRAM 13       /* SVD entropy: fp64 Gram matrix (fp64 MFMA) */
 #define MUON_KCLASS_SPEC_HOUSE 14      /* SVD entropy: Householder reflector per column */
-#define MUON_KCLASS_SPEC_PASS 15       /* SVD entropy: trailing update + matrix-vector product */
-#define MUON_KCLASS_SPEC_BISECT 16     /* SVD entropy: eigenvalues by Sturm bisection */
-#define MUON_KCLASS_SPEC_ENTROPY 17    /* SVD entropy: normalisation and entropy */
-#define MUON_KCLASS_COUNT 18
+#define MUON_KCLASS_SPEC_PASS 15       /* SVD entropy: trailing update + matrix-vector partials */
+#define MUON_KCLASS_SPEC_REDUCE 16     /* SVD entropy: matrix-vector product from the partials */
+#define MUON_KCLASS_SPEC_BISECT 17     /* SVD entropy: eigenvalues by Sturm bisection */
+#define MUON_KCLASS_SPEC_ENTROPY 18    /* SVD entropy: normalisation and entropy */
+#define MUON_KCLASS_COUNT 19
 
 /* Returns MUON_ABI_VERSION. Host only. */
 int muon_abi_version(void);
@@ -221,11 +222,12 @@ int adamw_step(const adamw_param* params, int32_t count, const adamw_hparams* hp
  * Computed in fp64 on the device: sigma_i^2 are the eigenvalues of the Gram matrix
  * X X^T (X = W, or W^T when A > B), reduced to tridiagonal form by Householder
  * reflections and solved by Sturm-count bisection. The cost is about
- * 2 min(A,B)^2 max(A,B) fp64 MFMA flops plus 16 min(A,B)^3 / 3 bytes of memory
- * traffic, so this is an occasional diagnostic, not a per-step call. */
+ * min(A,B)^2 max(A,B) fp64 MFMA flops plus 8 min(A,B)^3 / 3 bytes of memory traffic
+ * (the upper triangle of the shrinking trailing block, read and written once per
+ * column), so this is an occasional diagnostic, not a per-step call. */
 
 /* Workspace in bytes for svd_entropy on `count` matrices of shapes rows[i] x cols[i]
- * (about 8 min(A,B)^2 bytes per matrix for up to 16 matrices at a time). Host only.
+ * (about 8.25 min(A,B)^2 bytes per matrix for up to 16 matrices at a time). Host only.
  * Errors: INVALID_ARG (NULL bytes, count < 0, NULL rows/cols with count > 0, negative
  * dims), TOO_LARGE (as muon_workspace_bytes, or min(A, B) above 65536). */
 int svd_entropy_workspace_bytes(const int64_t* rows, const int64_t* cols, int32_t count, size_t* bytes);

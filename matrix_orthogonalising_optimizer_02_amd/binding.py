@@ -27,8 +27,8 @@ SCALE_RMS = 2       # 0.2 / RMS(O), Eq. 6
 
 KCLASS_NAMES = ("cast", "frob", "gram", "poly", "apply", "apply_final", "rownorm_rows",
                 "colnorm_partial", "colnorm_finalize", "colnorm_apply", "rms_finalize",
-                "scaled_update", "adamw", "spec_gram", "spec_house", "spec_pass", "spec_bisect",
-                "spec_entropy")
+                "scaled_update", "adamw", "spec_gram", "spec_house", "spec_pass", "spec_reduce",
+                "spec_bisect", "spec_entropy")
 
 EXPORTED = ("muon_abi_version", "muon_status_str", "muon_last_error", "muon_default_hparams",
             "muon_workspace_bytes", "muon_step", "ns5_batched", "rownorm_update",

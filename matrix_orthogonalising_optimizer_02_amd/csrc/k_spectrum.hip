@@ -10,15 +10,18 @@
 //   k_sp_house    column step j of the Householder tridiagonalisation: finishes the
 //                 previous step's w, forms column j of the current matrix, the diagonal
 //                 and sub-diagonal entries d_j, e_j, and the reflector (v_j, tau_j).
-//   k_sp_pass     one sweep over the trailing block: applies the previous step's
-//                 rank-2 update A <- A - v w^T - w v^T and, from the updated values,
-//                 p_j = tau_j A v_j. Read and written once per step: HBM-bound.
+//   k_sp_pass     one sweep over the upper triangle of the trailing block, in 64 x 64
+//                 tiles: applies the previous step's rank-2 update
+//                 A <- A - v w^T - w v^T and, from the updated values, each tile's row
+//                 sums of A v_j and (A symmetric) its column sums, into partial arrays.
+//                 The upper triangle is read and written once per step: HBM-bound.
+//   k_sp_reduce   p_j = tau_j A v_j from the tile partials, in a fixed order.
 //   k_sp_bisect   eigenvalue k of the tridiagonal matrix by bisection on Sturm counts,
 //                 one thread per eigenvalue, from the Gershgorin interval.
 //   k_sp_entropy  normalisation, entropy, and the optional sigma^2 output.
 // The rank-2 update is evaluated without contraction in a form that is symmetric in
-// its two indices, so the trailing block stays exactly symmetric and row j can stand
-// in for column j.
+// its two indices. Only the upper triangle of the trailing block is kept current, so
+// row j (contiguous) is read where the method needs column j.
 #include <float.h>
 
 #include "launch.hpp"
@@ -237,64 +240,124 @@ __global__ __launch_bounds__(1024) void k_sp_house(SpArgs args) {
 }
 
 // -------------------------------------------------------- trailing sweep ----
-// Rows r in [j+1, m) of matrix blockIdx.y, 4 per wave, 16 per block; each lane walks
-// the row in 16-byte pairs (c even; the pair straddling j+1 or m is masked).
-//   A[r][c] <- A[r][c] - (v_r w_c + w_r v_c)     (previous step's update, j > 0)
-//   p_r = tau_j sum_c A[r][c] v_j[c]
+// Tile (I, J), I <= J, of the absolute 64 x 64 tiling over rows/columns [j+1, m) of
+// matrix blockIdx.y; element (r, c) takes part iff j < r <= c < m. Thread t holds the
+// column pair c = 64 J + 2 (t % 32) + {0, 1} on rows 64 I + t / 32 + 8 k, k < 8.
+//   A[r][c] <- A[r][c] - (v_r w_c + w_r v_c)   (previous step's update, j > 0; stored)
+//   rowpart[I][J][r % 64] = sum_c A[r][c] x_c        (x = v_j; all c of the tile)
+//   colpart[I][J][c % 64] = sum_{r < c} A[r][c] x_r  (the mirrored lower element)
+// Every tile of the active range writes all 64 entries of both partials (zeros where
+// masked), so the reduce kernel reads no stale partial.
 __global__ __launch_bounds__(256) void k_sp_pass(SpArgs args) {
+    __shared__ double red[8][kSpPassTile];
     const SpDesc& d = args.d[blockIdx.y];
     const int j = args.j, m = d.m;
     if (j > m - 2) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r0 = j + 1 + blockIdx.x * kSpRowsPerBlock + wave * 4;
-    if (r0 >= m) return;
+    const int t0 = (j + 1) / kSpPassTile, tm = (m + kSpPassTile - 1) / kSpPassTile, nt = tm - t0;
+    int local = blockIdx.x;
+    if (local >= nt * (nt + 1) / 2) return;  // uniform per block
+    int I = t0, len = nt;
+    while (local >= len) {
+        local -= len;
+        ++I;
+        --len;
+    }
+    const int J = I + local;
+    const int tid = threadIdx.x, cp = tid & 31, rg = tid >> 5;
     const bool upd = j > 0;
     const double* vp = d.v[(j + 1) & 1];
-    const double* vcur = d.v[j & 1];
+    const double* x = d.v[j & 1];
     const double* wv = d.wv;
-    const double tau = d.tau[j & 1];
     const int64_t ld = d.ld;
-    double vr[4], wr[4], acc[4];
-    bool rv[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int r = r0 + t;
-        rv[t] = r < m;
-        vr[t] = (upd && rv[t]) ? vp[r] : 0.0;
-        wr[t] = (upd && rv[t]) ? wv[r] : 0.0;
-        acc[t] = 0.0;
-    }
     const int c0 = j + 1;
-    // c even and c < m <= ld, so the pair (c, c + 1) lies inside the padded row.
-    for (int c = (c0 & ~1) + 2 * lane; c < m; c += 128) {
-        const bool ok0 = c >= c0, ok1 = c + 1 < m;
-        const doublex2 x = *reinterpret_cast<const doublex2*>(vcur + c);
-        doublex2 vcol = {0.0, 0.0}, wcol = {0.0, 0.0};
+    const int c = J * kSpPassTile + 2 * cp;  // even, c + 1 < m_p
+    const bool cok0 = c >= c0 && c < m, cok1 = c + 1 >= c0 && c + 1 < m;
+    const doublex2 xc = *reinterpret_cast<const doublex2*>(x + c);
+    doublex2 vcol = {0.0, 0.0}, wcol = {0.0, 0.0};
+    if (upd) {
+        vcol = *reinterpret_cast<const doublex2*>(vp + c);
+        wcol = *reinterpret_cast<const doublex2*>(wv + c);
+    }
+    double col0 = 0.0, col1 = 0.0, rowp[8];
+    const int rbase = I * kSpPassTile + rg;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int r = rbase + 8 * k;
+        rowp[k] = 0.0;
+        if (r < c0 || r >= m) continue;
+        const bool e0 = cok0 && c >= r, e1 = cok1 && c + 1 >= r;
+        if (!(e0 || e1)) continue;
+        double* row = d.s + (int64_t)r * ld + c;
+        doublex2 a = *reinterpret_cast<const doublex2*>(row);
         if (upd) {
-            vcol = *reinterpret_cast<const doublex2*>(vp + c);
-            wcol = *reinterpret_cast<const doublex2*>(wv + c);
+            const double vr = vp[r], wr = wv[r];
+            a.x = rank2_sub(a.x, vr, wcol.x, wr, vcol.x);
+            a.y = rank2_sub(a.y, vr, wcol.y, wr, vcol.y);
+            if (e0 && e1) *reinterpret_cast<doublex2*>(row) = a;
+            else if (e0) row[0] = a.x;
+            else row[1] = a.y;
         }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            if (!rv[t]) continue;
-            double* row = d.s + (int64_t)(r0 + t) * ld + c;
-            doublex2 a = *reinterpret_cast<const doublex2*>(row);
-            if (upd) {
-                a.x = rank2_sub(a.x, vr[t], wcol.x, wr[t], vcol.x);
-                a.y = rank2_sub(a.y, vr[t], wcol.y, wr[t], vcol.y);
-                if (ok0 && ok1) *reinterpret_cast<doublex2*>(row) = a;
-                else if (ok0) row[0] = a.x;
-                else if (ok1) row[1] = a.y;
-            }
-            if (ok0) acc[t] += a.x * x.x;
-            if (ok1) acc[t] += a.y * x.y;
+        const double xr = x[r];
+        if (e0) {
+            rowp[k] += a.x * xc.x;
+            if (c > r) col0 += a.x * xr;
+        }
+        if (e1) {
+            rowp[k] += a.y * xc.y;
+            if (c + 1 > r) col1 += a.y * xr;
         }
     }
+    const int64_t pbase = ((int64_t)I * d.tp + J) * kSpPassTile;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const double s = wave_sum_d(acc[t]);
-        if (lane == 0 && rv[t]) d.p[r0 + t] = tau * s;
+    for (int k = 0; k < 8; ++k) {
+        double v = rowp[k];
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);  // the 32 lanes of one row
+        if (cp == 0) d.rowpart[pbase + rg + 8 * k] = v;
     }
+    red[rg][2 * cp] = col0;
+    red[rg][2 * cp + 1] = col1;
+    __syncthreads();
+    if (tid < kSpPassTile) {
+        double v = 0.0;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) v += red[g][tid];
+        d.colpart[pbase + tid] = v;
+    }
+}
+
+// p_r = tau_j (sum_{J >= I} rowpart[I][J][r % 64] + sum_{t0 <= I' <= I} colpart[I'][I][r % 64])
+// for rows r in [j+1, m), I = r / 64: row sums of the tiles right of the diagonal and
+// column sums of the tiles above it, J and I' ascending.
+__global__ __launch_bounds__(256) void k_sp_reduce(SpArgs args) {
+    const SpDesc& d = args.d[blockIdx.y];
+    const int j = args.j, m = d.m;
+    const int r = j + 1 + blockIdx.x * 256 + threadIdx.x;
+    if (j > m - 2 || r >= m) return;
+    const int t0 = (j + 1) / kSpPassTile, tm = (m + kSpPassTile - 1) / kSpPassTile;
+    const int I = r / kSpPassTile, lr = r % kSpPassTile;
+    // four independent chains (J and I' ascending within each), combined at the end
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    const double* rp = d.rowpart + (int64_t)I * d.tp * kSpPassTile + lr;  // + J * 64
+    int J = I;
+    for (; J + 4 <= tm; J += 4) {
+        s0 += rp[(int64_t)J * kSpPassTile];
+        s1 += rp[(int64_t)(J + 1) * kSpPassTile];
+        s2 += rp[(int64_t)(J + 2) * kSpPassTile];
+        s3 += rp[(int64_t)(J + 3) * kSpPassTile];
+    }
+    for (; J < tm; ++J) s0 += rp[(int64_t)J * kSpPassTile];
+    const double* cq = d.colpart + (int64_t)I * kSpPassTile + lr;  // + I' * tp * 64
+    const int64_t cs = (int64_t)d.tp * kSpPassTile;
+    int I2 = t0;
+    for (; I2 + 4 <= I + 1; I2 += 4) {
+        s0 += cq[I2 * cs];
+        s1 += cq[(I2 + 1) * cs];
+        s2 += cq[(I2 + 2) * cs];
+        s3 += cq[(I2 + 3) * cs];
+    }
+    for (; I2 <= I; ++I2) s0 += cq[I2 * cs];
+    d.p[r] = d.tau[j & 1] * ((s0 + s1) + (s2 + s3));
 }
 
 // ------------------------------------------------------------- bisection ----
@@ -412,9 +475,13 @@ hipError_t launch_sp_house(const SpArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_sp_pass(const SpArgs& a, int max_trailing, hipStream_t s) {
-    const int bx = (max_trailing + kSpRowsPerBlock - 1) / kSpRowsPerBlock;
-    hipLaunchKernelGGL(k_sp_pass, dim3(bx, a.n), dim3(256), 0, s, a);
+hipError_t launch_sp_pass(const SpArgs& a, int max_tiles, hipStream_t s) {
+    hipLaunchKernelGGL(k_sp_pass, dim3(max_tiles, a.n), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_sp_reduce(const SpArgs& a, int max_trailing, hipStream_t s) {
+    hipLaunchKernelGGL(k_sp_reduce, dim3((max_trailing + 255) / 256, a.n), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -194,12 +194,14 @@ struct AdamArgs {
 // For X = W (rows <= cols) or W^T (rows > cols), [m, n], the eigenvalues of the Gram
 // matrix S = X X^T are sigma_i^2. S (m_p x m_p, m_p = m rounded up to kSpTile, zero
 // padding) is reduced to tridiagonal form by Householder reflections, one column per
-// step: step j's house kernel forms reflector v_j from column j (after the previous
-// step's rank-2 update, applied on the fly) and the pass kernel applies that update
-// to the trailing block while computing p_j = tau_j S v_j in the same sweep. The
+// step: step j's house kernel forms reflector v_j from row j (after the previous step's
+// rank-2 update, applied on the fly); the pass kernel applies that update to the upper
+// triangle of the trailing block, tile by tile, and leaves per-tile row and column sums
+// of A v_j, which the reduce kernel adds in a fixed order into p_j = tau_j A v_j. Only
+// the upper triangle is kept current (the lower one is stale after step 0). The
 // eigenvalues of the tridiagonal matrix come from Sturm-count bisection.
 constexpr int kSpTile = 128;        // Gram block tile (4 waves of 64 x 64)
-constexpr int kSpRowsPerBlock = 16; // pass kernel: 4 waves x 4 rows
+constexpr int kSpPassTile = 64;     // pass kernel tile (upper-triangle tiles of the trailing block)
 constexpr int kSpBisectIters = 80;  // bound on bisection halvings (stops earlier)
 
 struct SpDesc {
@@ -215,6 +217,9 @@ struct SpDesc {
     double* v[2];          // Householder vectors v_j in v[j & 1] (entries j+1 .. m-1)
     double* wv;            // w_{j-1} = p_{j-1} - (tau_{j-1} / 2) (p_{j-1} . v_{j-1}) v_{j-1}
     double* p;             // p_j = tau_j S^(j) v_j
+    double* rowpart;       // pass partials [tp][tp][64]: tile (I, J) row sums of A v
+    double* colpart;       // pass partials [tp][tp][64]: tile (I, J) column sums (mirror)
+    int32_t tp;            // partial-array tile dimension, m_p / kSpPassTile
     double* d;             // tridiagonal: diagonal (m)
     double* e;             // tridiagonal: sub-diagonal (m - 1)
     double* lam;           // eigenvalues, ascending (m)
@@ -249,7 +254,8 @@ hipError_t launch_adamw(const AdamArgs& a, hipStream_t s);
 hipError_t launch_scaled_update(const UpdArgs& a, hipStream_t s);
 hipError_t launch_sp_gram(const SpArgs& a, hipStream_t s);
 hipError_t launch_sp_house(const SpArgs& a, hipStream_t s);
-hipError_t launch_sp_pass(const SpArgs& a, int max_trailing, hipStream_t s);
+hipError_t launch_sp_pass(const SpArgs& a, int max_tiles, hipStream_t s);
+hipError_t launch_sp_reduce(const SpArgs& a, int max_trailing, hipStream_t s);
 hipError_t launch_sp_bisect(const SpArgs& a, int max_m, hipStream_t s);
 hipError_t launch_sp_entropy(const SpArgs& a, hipStream_t s);
 

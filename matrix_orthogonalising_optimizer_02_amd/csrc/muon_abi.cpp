@@ -584,7 +584,8 @@ int do_rownorm(const muon_matrix* mats, int32_t count, const muon_hparams* hp, v
 
 // ------------------------------------------------------ singular spectrum ----
 // SVD-entropy diagnostic ("Muon is Scalable", Sec. 3.4). Per matrix: the fp64 Gram
-// matrix S (m_p x m_p), seven m_p vectors (v_j twice, w, p, d, e, eigenvalues) and
+// matrix S (m_p x m_p), seven m_p vectors (v_j twice, w, p, d, e, eigenvalues), the
+// pass kernel's two partial arrays (tp x tp tiles of 64 doubles, tp = m_p / 64) and
 // tau; groups of up to kMaxGroup matrices (largest m first) share one workspace
 // region and run one after another.
 constexpr int64_t kSpMaxM = 65536;
@@ -606,7 +607,13 @@ struct SpPlan {
 };
 
 size_t sp_vec_bytes(int64_t m_p) { return align256(size_t(m_p) * 8); }
-size_t sp_mat_bytes(int64_t m_p) { return align256(size_t(m_p) * size_t(m_p) * 8) + 7 * sp_vec_bytes(m_p) + 256; }
+size_t sp_part_bytes(int64_t m_p) {
+    const size_t tp = size_t(m_p / kSpPassTile);
+    return align256(tp * tp * kSpPassTile * 8);
+}
+size_t sp_mat_bytes(int64_t m_p) {
+    return align256(size_t(m_p) * size_t(m_p) * 8) + 7 * sp_vec_bytes(m_p) + 2 * sp_part_bytes(m_p) + 256;
+}
 
 int make_sp_plan(const int64_t* rows, const int64_t* cols, int32_t count, SpPlan* plan) {
     if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count < 0");
@@ -673,6 +680,11 @@ int run_spectrum(const std::vector<SpMat>& g, const float* const* w, char* ws, d
             *v = reinterpret_cast<double*>(base);
             base += sp_vec_bytes(sm.m_p);
         }
+        d.rowpart = reinterpret_cast<double*>(base);
+        base += sp_part_bytes(sm.m_p);
+        d.colpart = reinterpret_cast<double*>(base);
+        base += sp_part_bytes(sm.m_p);
+        d.tp = int32_t(sm.m_p / kSpPassTile);
         d.tau = reinterpret_cast<double*>(base);
         d.entropy = entropy + sm.idx;
         tiles += sm.tm * (sm.tm + 1) / 2;
@@ -686,8 +698,17 @@ int run_spectrum(const std::vector<SpMat>& g, const float* const* w, char* ws, d
         rc = run_kernel(MUON_KCLASS_SPEC_HOUSE, s, "spectrum house", [&] { return launch_sp_house(a, s); });
         if (rc) return rc;
         if (j <= max_m - 2) {
+            int max_tiles = 0;
+            for (const SpMat& sm : g) {
+                if (j > sm.m - 2) continue;
+                const int nt = (sm.m + kSpPassTile - 1) / kSpPassTile - (j + 1) / kSpPassTile;
+                max_tiles = std::max(max_tiles, nt * (nt + 1) / 2);
+            }
             rc = run_kernel(MUON_KCLASS_SPEC_PASS, s, "spectrum pass",
-                            [&] { return launch_sp_pass(a, max_m - j - 1, s); });
+                            [&] { return launch_sp_pass(a, max_tiles, s); });
+            if (rc) return rc;
+            rc = run_kernel(MUON_KCLASS_SPEC_REDUCE, s, "spectrum reduce",
+                            [&] { return launch_sp_reduce(a, max_m - j - 1, s); });
             if (rc) return rc;
         }
     }

@@ -295,10 +295,12 @@ def test_svd_entropy_workspace_planning(lib):
     assert B.svd_entropy_workspace_bytes([]) == 0
     assert B.svd_entropy_workspace_bytes([(0, 5), (7, 0)]) == 0
     one = B.svd_entropy_workspace_bytes([(100, 300)])
-    assert one >= 128 * 128 * 8 + 7 * 128 * 8  # fp64 Gram padded to 128, seven vectors
+    # fp64 Gram padded to 128, seven vectors, two partial arrays of (128 / 64)^2 tiles x 64
+    assert one >= 128 * 128 * 8 + 7 * 128 * 8 + 2 * 4 * 64 * 8
     assert B.svd_entropy_workspace_bytes([(300, 100)]) == one  # orientation-free
     big = B.svd_entropy_workspace_bytes([(5120, 30720)] * 10)
-    assert 10 * 5120 * 5120 * 8 <= big < 10 * 5120 * 5120 * 8 + (1 << 22)
+    per = 5120 * 5120 * 8 + 2 * 80 * 80 * 64 * 8  # Gram + partials (80 x 80 tiles)
+    assert 10 * per <= big < 10 * per + (1 << 22)
     many = B.svd_entropy_workspace_bytes([(256, 512)] * 20)  # two groups, region reused
     assert many == B.svd_entropy_workspace_bytes([(256, 512)] * 16)
     with pytest.raises(B.MuonError) as e:
