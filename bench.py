@@ -227,7 +227,7 @@ def measure_adamw(pkg, torch, dev, wl, n, say):
     return res
 
 
-def measure_spectrum(pkg, torch, weights, n, say):
+def measure_spectrum(pkg, torch, weights, n, say, cpu=True):
     """The SVD-entropy diagnostic over the layer set's weights, fp64 on the device.
 
     Algorithmic work per matrix (m = min, n = max): the Gram kernel's m (m + 1) n
@@ -268,9 +268,43 @@ def measure_spectrum(pkg, torch, weights, n, say):
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(pass_bytes / (pass_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                 "avg_launch_ms": round(per["pass"][0] / max(per["pass"][1], 1), 4)}}
+    if cpu:
+        res["cpu_oracle"] = spectrum_oracle_time(weights, shapes)
     say(f"spectrum: {res}")
     del ws
     return res
+
+
+def spectrum_oracle_time(weights, shapes):
+    """The float64 oracle (library SVD, singular values only) on the set's smallest
+    matrix, scaled to the set by the Golub-Kahan bidiagonalisation count
+    4 m^2 n - 4 m^3 / 3 (m = min, n = max); the host's BLAS threads."""
+    import numpy as np
+    from oracle import spectrum_oracle as SO
+
+    idx = min(range(len(shapes)), key=lambda i: shapes[i][0] * shapes[i][1])
+    x = weights[idx].cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    SO.svd_entropy(x)
+    t = time.perf_counter() - t0
+
+    def cost(s):
+        mm, nn = float(min(s)), float(max(s))
+        return 4.0 * mm * mm * nn - 4.0 * mm ** 3 / 3.0
+
+    total = t * sum(cost(s) for s in shapes) / cost(shapes[idx])
+    return {"seconds_per_call": round(total, 1), "sample_seconds": round(t, 2),
+            "sample": f"oracle SVD entropy of the {shapes[idx][0]}x{shapes[idx][1]} matrix, scaled by "
+                      f"4 m^2 n - 4 m^3 / 3 to the {len(shapes)}-matrix set",
+            "cores": _blas_threads()}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([d.get("num_threads", 1) for d in threadpool_info()] or [1]))
+    except Exception:
+        return len(os.sched_getaffinity(0))
 
 
 def main():
@@ -354,7 +388,8 @@ def main():
     variants = measure_variants(pkg, torch, weights, momenta, grads, ws, k, wl, args.variant_steps, say) \
         if args.variant_steps > 0 else None
     hybrid = measure_adamw(pkg, torch, dev, wl, args.adamw_steps, say) if args.adamw_steps > 0 else None
-    spectrum = measure_spectrum(pkg, torch, weights, args.spectrum_calls, say) if args.spectrum_calls > 0 else None
+    spectrum = measure_spectrum(pkg, torch, weights, args.spectrum_calls, say, not args.no_cpu_baseline) \
+        if args.spectrum_calls > 0 else None
 
     refreshes = args.steps
     rownorm_steps = args.steps * (k - 1)
