@@ -211,7 +211,7 @@ struct SpDesc {
     int32_t tall;          // rows > cols: X = W^T
     int32_t tm;            // Gram tiles per side, ceil(m / kSpTile)
     int32_t tile_begin;    // first Gram tile of this matrix in the launch
-    int32_t sigma_off;     // offset of this matrix's values in sigma_sq (if any)
+    int64_t sigma_off;     // offset of this matrix's values in sigma_sq (if any)
     int64_t ld;            // leading dimension of s (m_p)
     double* s;             // symmetric work matrix, m_p x m_p
     double* v[2];          // Householder vectors v_j in v[j & 1] (entries j+1 .. m-1)

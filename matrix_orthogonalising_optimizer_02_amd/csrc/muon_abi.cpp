@@ -670,7 +670,7 @@ int run_spectrum(const std::vector<SpMat>& g, const float* const* w, char* ws, d
         d.tall = sm.tall ? 1 : 0;
         d.tm = sm.tm;
         d.tile_begin = tiles;
-        d.sigma_off = int32_t(sm.sigma_off);
+        d.sigma_off = sm.sigma_off;
         d.ld = sm.m_p;
         char* base = ws + sm.off;
         d.s = reinterpret_cast<double*>(base);
