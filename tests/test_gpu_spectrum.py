@@ -13,9 +13,9 @@ taken 10x looser.
 Cases: flat, tall and square shapes with ragged tails around the 128 Gram tile and
 the 16-wide K slice; a flat spectrum (entropy 1), rank one (entropy 0), two-level
 and power-law spectra, a zero matrix (NaN), a single singular value (0), more matrices
-than one launch group, empty matrices, determinism, and the full-size 5120 x 5120
-matrix of the 15B-scale layer set together with the other nine in the launch the
-benchmark times.
+than one launch group, empty matrices, determinism, NaN / Inf inputs (NaN entropy for
+that matrix only), and the full-size 5120 x 5120 matrix of the 15B-scale layer set
+together with the other nine in the launch the benchmark times.
 """
 import math
 import sys
@@ -173,3 +173,20 @@ def test_full_size_layer_set(torch_dev):
             check([x.astype(np.float32)], ent[i:i + 1], lam, H_TOL_FULL, LAM_TOL_FULL, label="full 5120^2")
         off += n
     log(f"full-size entropies: {np.round(ent, 6).tolist()}")
+
+
+def test_nan_and_inf_propagate_per_matrix(torch_dev):
+    """A NaN or Inf in one matrix gives that matrix a NaN entropy and NaN sigma^2; the
+    other matrices of the same launch are unaffected."""
+    torch, dev = torch_dev
+    good = WL.host_normal(606, WL.ROLE_W, 0, (150, 260), 0.02)
+    bad_nan = WL.host_normal(606, WL.ROLE_W, 1, (140, 90), 0.02)
+    bad_nan[7, 11] = np.nan
+    bad_inf = WL.host_normal(606, WL.ROLE_W, 2, (64, 200), 0.02)
+    bad_inf[3, 5] = np.inf
+    mats = [good, bad_nan, bad_inf]
+    ent, sig = run(torch, dev, mats)
+    assert math.isnan(ent[1]) and math.isnan(ent[2])
+    # no finite sigma^2 survives (NaN, or Inf where the Gershgorin bound is infinite)
+    assert not np.any(np.isfinite(sig[150:150 + 90])) and not np.any(np.isfinite(sig[240:240 + 64]))
+    check([good], ent[:1], sig[:150], label="beside NaN / Inf matrices")
