@@ -94,6 +94,8 @@ def parse():
                     help="timed AdamW steps over the model's AdamW group (0: skip)")
     ap.add_argument("--spectrum-calls", type=int, default=1,
                     help="timed SVD-entropy diagnostic calls over the layer set (0 = skip)")
+    ap.add_argument("--shard-degree", type=int, default=8,
+                    help="time one GPU's share of the row-sharded RowNorm step at this degree (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
@@ -320,6 +322,57 @@ def _blas_threads():
         return len(os.sched_getaffinity(0))
 
 
+def measure_shard_rownorm(pkg, torch, dev, wl, degree, reps, rn_ms, say):
+    """One GPU's share of the RowNorm step with the weights sharded by rows over `degree`
+    GPUs: every matrix [A, B] contributes its block [A / degree, B]. Flat blocks take
+    rownorm_update (their rows are whole); tall blocks take rownorm_shard_colsq, the
+    all-reduce of the column sums (identity here: one GPU), and rownorm_shard_apply."""
+    from matrix_orthogonalising_optimizer_02_amd import workloads as WL
+
+    shapes = [(a // degree, b) for a, b in wl.shapes]
+    tall = [a > b for a, b in wl.shapes]
+    blk = []
+    for i, (s, t) in enumerate(zip(shapes, tall)):
+        w = torch.empty(s, dtype=torch.float32, device=dev)
+        m = torch.zeros(s, dtype=torch.float32, device=dev)
+        g = torch.empty(s, dtype=torch.float32, device=dev)
+        WL.device_fill(w, wl.key, WL.ROLE_W, i, wl.w_std)
+        WL.device_fill(g, wl.key, WL.ROLE_G, i, wl.g_std, wl.g_dist)
+        blk.append((w, m, g, t, wl.shapes[i][0]))
+    hp = pkg.default_hparams(period_k=3)
+    flat = [b for b in blk if not b[3]]
+    tl = [b for b in blk if b[3]]
+    ws_flat = pkg.make_workspace([tuple(b[0].shape) for b in flat], dev)
+    full = [b[4] for b in tl]
+    nb = pkg.rownorm_shard_workspace_bytes([tuple(b[0].shape) for b in tl], full)
+    ws_tall = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    colsq = [torch.empty(b[0].shape[1], dtype=torch.float32, device=dev) for b in tl]
+
+    def share_step():
+        pkg.rownorm_update([b[0] for b in flat], [b[1] for b in flat], [b[2] for b in flat], hp, ws_flat)
+        pkg.rownorm_shard_colsq([b[0] for b in tl], [b[1] for b in tl], [b[2] for b in tl], full, colsq, hp, ws_tall)
+        pkg.rownorm_shard_apply([b[0] for b in tl], [b[1] for b in tl], full, colsq, hp, ws_tall)  # identity reduce
+
+    share_step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        share_step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    elems = sum(x * y for x, y in shapes)
+    res = {"degree": degree, "block_shapes": [list(x) for x in shapes], "elements": elems,
+           "share_step_ms": round(ms, 4), "share_gbs": round(20.0 * elems / (ms * 1e-3) / 1e9, 1),
+           "unsharded_rownorm_ms_over_degree": round(rn_ms / degree, 4),
+           "share_vs_ideal": round((rn_ms / degree) / ms, 3),
+           "note": "tall blocks: column sums, identity all-reduce (one GPU), then the update"}
+    say(f"shard: {res}")
+    del blk, ws_flat, ws_tall
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -413,6 +466,8 @@ def main():
     ns5_tflops = ns5_flops / (ns5_ms * 1e-3) / 1e12
     rn_ms = (ms["rownorm_rows"] + ms["colnorm_partial"] + ms["colnorm_finalize"] + ms["colnorm_apply"]) / rownorm_steps
     rn_gbs = 20.0 * wl.elements / (rn_ms * 1e-3) / 1e9
+    shard = measure_shard_rownorm(pkg, torch, dev, wl, args.shard_degree, 10, rn_ms, say) \
+        if args.shard_degree > 1 else None
     # dominant kernel: the B X product of iterations 1..N-1
     apply_launch_ms = ms["apply"] / max(cnt["apply"], 1)
     apply_launch_flops = sum(apply_flops(min(s), max(s)) for s in shapes)
@@ -489,6 +544,8 @@ def main():
         out["hybrid"] = hybrid
     if spectrum is not None:
         out["spectrum"] = spectrum
+    if shard is not None:
+        out["shard_rownorm"] = shard
     if not args.no_cpu_baseline:
         say("cpu baseline: timing the float64 oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(wl, k)

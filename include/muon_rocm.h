@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 3
+#define MUON_ABI_VERSION 4
 
 /* Status codes returned by every entry point. */
 #define MUON_OK 0
@@ -171,6 +171,49 @@ int ns5_batched(const float* const* m_in, float* const* o_out, const int64_t* ro
  * hp->period_k is not used. Errors as muon_step. */
 int rownorm_update(const muon_matrix* mats, int32_t count, const muon_hparams* hp,
                    void* workspace, size_t workspace_bytes, float* update_rms, void* stream);
+
+/* ---- One GPU's share of a row-sharded RowNorm step --------------------------------
+ * "Scaling Muon for Diffusion Transformers", distributed-implementation paragraph: with
+ * the weights sharded by rows (dim 0) across GPUs, the rows of a flat matrix (A <= B)
+ * are whole on every GPU, so rownorm_update() on a GPU's block of rows is already its
+ * share of the step (the block's sqrt(max(rows, B)) = sqrt(B) is the whole matrix's
+ * scale). A tall matrix (A > B) normalises columns, which span the GPUs. Its step is
+ * split in two calls around the caller's reduction:
+ *   1. rownorm_shard_colsq: M <- mu M + G on the block, and colsq[c] = sum over the
+ *      block's rows of M[r][c]^2;
+ *   2. the caller sums colsq over the GPUs holding the matrix (an all-reduce; with
+ *      one block per matrix, nothing);
+ *   3. rownorm_shard_apply: W <- W - lr (c gamma M / max(sqrt(total[c]), eps) + wd W)
+ *      with c = rms_scale sqrt(full_rows), or rms_scale sqrt(hidden) under
+ *      MUON_SCALE_HIDDEN (MUON_SCALE_RMS takes the max-dimension form, as rownorm_update).
+ * Concatenating the blocks reproduces rownorm_update() on the whole matrix up to the
+ * summation order of the column sums. */
+typedef struct muon_shard {
+    int64_t rows, cols;  /* this GPU's block: `rows` rows of the matrix, all `cols` columns */
+    int64_t full_rows;   /* A of the whole matrix: must exceed cols (tall) and be >= rows */
+    float* w;            /* [rows, cols] block of W, updated by rownorm_shard_apply */
+    float* m;            /* [rows, cols] block of M, updated by rownorm_shard_colsq */
+    const float* g;      /* [rows, cols] block of G, read by rownorm_shard_colsq (apply: unused, may be NULL) */
+} muon_shard;
+
+/* Workspace in bytes for either shard call on these blocks (about 4 cols ceil(rows / 256)
+ * bytes per block for up to 16 blocks at a time). Host only.
+ * Errors: INVALID_ARG (NULL bytes or shards, count < 0, negative dims, full_rows <= cols,
+ * rows > full_rows), TOO_LARGE. Blocks with cols == 0 are skipped. */
+int rownorm_shard_workspace_bytes(const muon_shard* shards, int32_t count, size_t* bytes);
+
+/* Step 1 for `count` blocks (host array). colsq: host array of `count` DEVICE pointers,
+ * each to cols floats (4-byte aligned), written; a block with rows == 0 writes zeros.
+ * Errors: as rownorm_update, plus INVALID_ARG for NULL colsq entries. */
+int rownorm_shard_colsq(const muon_shard* shards, int32_t count, const muon_hparams* hp,
+                        float* const* colsq, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Step 3. colsq_total: host array of `count` DEVICE pointers to the reduced column sums
+ * (cols floats each), read only. M must hold step 1's output. Blocks with rows == 0 are
+ * left alone. Errors: as rownorm_shard_colsq. */
+int rownorm_shard_apply(const muon_shard* shards, int32_t count, const muon_hparams* hp,
+                        const float* const* colsq_total, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* ---- AdamW companion for the parameters Muon does not take -------------------------
  * "Scaling Muon for Diffusion Transformers" (setup paragraph) keeps biases,

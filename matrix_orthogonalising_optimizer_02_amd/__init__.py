@@ -20,6 +20,9 @@ from .binding import (  # noqa: F401
     make_workspace,
     muon_step,
     ns5_batched,
+    rownorm_shard_apply,
+    rownorm_shard_colsq,
+    rownorm_shard_workspace_bytes,
     rownorm_update,
     svd_entropy,
     svd_entropy_workspace_bytes,

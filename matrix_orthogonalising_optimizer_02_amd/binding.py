@@ -33,6 +33,7 @@ KCLASS_NAMES = ("cast", "frob", "gram", "poly", "apply", "apply_final", "rownorm
 EXPORTED = ("muon_abi_version", "muon_status_str", "muon_last_error", "muon_default_hparams",
             "muon_workspace_bytes", "muon_step", "ns5_batched", "rownorm_update",
             "adamw_default_hparams", "adamw_step", "svd_entropy_workspace_bytes", "svd_entropy",
+            "rownorm_shard_workspace_bytes", "rownorm_shard_colsq", "rownorm_shard_apply",
             "muon_timing_enable", "muon_timing_read")
 
 
@@ -59,6 +60,11 @@ class AdamWHParams(ctypes.Structure):
 class AdamWParam(ctypes.Structure):
     _fields_ = [("numel", ctypes.c_int64), ("w", ctypes.c_void_p), ("m", ctypes.c_void_p),
                 ("v", ctypes.c_void_p), ("g", ctypes.c_void_p)]
+
+
+class MuonShard(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("full_rows", ctypes.c_int64),
+                ("w", ctypes.c_void_p), ("m", ctypes.c_void_p), ("g", ctypes.c_void_p)]
 
 
 class MuonError(RuntimeError):
@@ -102,10 +108,16 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                                 i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.svd_entropy.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
                                 i32, vp, sz, vp, vp, vp]
+    lib.rownorm_shard_workspace_bytes.argtypes = [ctypes.POINTER(MuonShard), i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.rownorm_shard_colsq.argtypes = [ctypes.POINTER(MuonShard), i32, ctypes.POINTER(MuonHParams),
+                                        ctypes.POINTER(vp), vp, sz, vp]
+    lib.rownorm_shard_apply.argtypes = [ctypes.POINTER(MuonShard), i32, ctypes.POINTER(MuonHParams),
+                                        ctypes.POINTER(vp), vp, sz, vp]
     lib.muon_timing_enable.argtypes = [ctypes.c_int]
     lib.muon_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     for name in ("muon_step", "ns5_batched", "rownorm_update", "muon_workspace_bytes", "adamw_step",
-                 "svd_entropy_workspace_bytes", "svd_entropy", "muon_timing_enable", "muon_timing_read"):
+                 "svd_entropy_workspace_bytes", "svd_entropy", "rownorm_shard_workspace_bytes",
+                 "rownorm_shard_colsq", "rownorm_shard_apply", "muon_timing_enable", "muon_timing_read"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -327,6 +339,84 @@ def adamw_step(params, grads, exp_avgs, exp_avg_sqs, step: int, hp: Optional[Ada
                stream=None):
     """One AdamW step (0-based `step`) over tensors of any shape, in place."""
     AdamWGroup(params, grads, exp_avgs, exp_avg_sqs, hp).step(step, stream)
+
+
+# ------------------------------------------------ row-sharded RowNorm share ----
+
+def _shards(weights, momenta, grads, full_rows):
+    n = len(weights)
+    if not (n == len(momenta) == len(full_rows)) or (grads is not None and len(grads) != n):
+        raise ValueError("weights, momenta, grads and full_rows must have the same length")
+    arr = (MuonShard * max(n, 1))()
+    for i in range(n):
+        w, m = weights[i], momenta[i]
+        g = grads[i] if grads is not None else None
+        for t, nm in ((w, "weight"), (m, "momentum")) + (((g, "grad"),) if g is not None else ()):
+            _check_tensor(t, f"{nm}[{i}]")
+        if w.shape != m.shape or (g is not None and g.shape != w.shape):
+            raise ValueError(f"shape mismatch at index {i}")
+        arr[i] = MuonShard(w.shape[0], w.shape[1], int(full_rows[i]), w.data_ptr() or None,
+                           m.data_ptr() or None, (g.data_ptr() or None) if g is not None else None)
+    return arr
+
+
+def rownorm_shard_workspace_bytes(shapes, full_rows) -> int:
+    arr = (MuonShard * max(len(shapes), 1))()
+    for i, (s, a) in enumerate(zip(shapes, full_rows)):
+        arr[i] = MuonShard(int(s[0]), int(s[1]), int(a), None, None, None)
+    out = ctypes.c_size_t(0)
+    _check(load_library().rownorm_shard_workspace_bytes(arr, len(shapes), ctypes.byref(out)),
+           "rownorm_shard_workspace_bytes")
+    return int(out.value)
+
+
+def _shard_ws(workspace, weights, full_rows, dev):
+    if workspace is None:
+        torch = _torch()
+        nb = rownorm_shard_workspace_bytes([tuple(w.shape) for w in weights], full_rows)
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    return ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel())
+
+
+def _sum_ptrs(tensors, weights, name):
+    torch = _torch()
+    ptrs = (ctypes.c_void_p * max(len(weights), 1))()
+    for i, (t, w) in enumerate(zip(tensors, weights)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 1 \
+                or not t.is_contiguous() or t.numel() != w.shape[1]:
+            raise ValueError(f"{name}[{i}] must be a contiguous float32 tensor of {w.shape[1]} entries")
+        ptrs[i] = t.data_ptr() or None
+    return ptrs
+
+
+def rownorm_shard_colsq(weights, momenta, grads, full_rows, colsq=None, hp: Optional[MuonHParams] = None,
+                        workspace=None, stream=None):
+    """Step 1 of a tall matrix's row-sharded RowNorm step on this GPU's blocks: momentum,
+    and the block's column sums of M'^2 (returned; reduce them across the GPUs)."""
+    torch = _torch()
+    hp = hp or default_hparams()
+    dev = weights[0].device if weights else None
+    if colsq is None:
+        colsq = [torch.empty(w.shape[1], dtype=torch.float32, device=dev) for w in weights]
+    arr = _shards(weights, momenta, grads, full_rows)
+    ws, wsb = _shard_ws(workspace, weights, full_rows, dev)
+    rc = load_library().rownorm_shard_colsq(arr, len(weights), ctypes.byref(hp), _sum_ptrs(colsq, weights, "colsq"),
+                                            ws, wsb, _stream_handle(stream, dev))
+    _check(rc, "rownorm_shard_colsq")
+    return colsq
+
+
+def rownorm_shard_apply(weights, momenta, full_rows, colsq_total, hp: Optional[MuonHParams] = None,
+                        workspace=None, stream=None):
+    """Step 3: the column-normalised update of this GPU's blocks from the reduced sums."""
+    hp = hp or default_hparams()
+    dev = weights[0].device if weights else None
+    arr = _shards(weights, momenta, None, full_rows)
+    ws, wsb = _shard_ws(workspace, weights, full_rows, dev)
+    rc = load_library().rownorm_shard_apply(arr, len(weights), ctypes.byref(hp),
+                                            _sum_ptrs(colsq_total, weights, "colsq_total"), ws, wsb,
+                                            _stream_handle(stream, dev))
+    _check(rc, "rownorm_shard_apply")
 
 
 # ------------------------------------------------------- spectrum diagnostic ----

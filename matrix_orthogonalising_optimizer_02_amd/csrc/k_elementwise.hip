@@ -370,6 +370,10 @@ __global__ __launch_bounds__(256) void k_colnorm_finalize(ColArgs args) {
     if (c >= d.cols) return;
     float s = 0.f;
     for (int k = 0; k < d.chunks; ++k) s += d.partial[(int64_t)k * d.cols + c];
+    if (args.sums_only) {  // a row block's share of a sharded matrix: the caller reduces
+        d.inv[c] = s;
+        return;
+    }
     const float den = max_keep_nan(sqrtf(s), args.eps);
     d.inv[c] = 1.0f / den;
     if (d.part) d.part[c] = s / (den * den);

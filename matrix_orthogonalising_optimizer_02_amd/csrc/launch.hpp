@@ -121,6 +121,7 @@ struct ColArgs {
     int32_t n;
     int32_t total;
     float mu, decay, eps;
+    int32_t sums_only;     // finalize: write the raw column sums of squares into `inv`
 };
 
 // ---- update RMS and the Eq. 6 scale -------------------------------------------

@@ -582,6 +582,96 @@ int do_rownorm(const muon_matrix* mats, int32_t count, const muon_hparams* hp, v
     return MUON_OK;
 }
 
+// ------------------------------------------------- row-sharded RowNorm share ----
+// One GPU's share of the RowNorm step of a tall matrix sharded by rows ([DiT]
+// distributed-implementation paragraph): the block's momentum update and column sums
+// of M'^2 (rownorm_shard_colsq), then, with the totals the caller reduced across the
+// GPUs, the column-normalised update (rownorm_shard_apply). Both reuse the tall RowNorm
+// kernels; the workspace holds per-shard chunk partials and inverse norms.
+struct ShardPlan {
+    int idx;
+    int64_t rows, cols, chunks;
+    size_t partial, inv;  // workspace offsets relative to the group base
+};
+
+int plan_shards(const muon_shard* shards, int32_t count, std::vector<std::vector<ShardPlan>>* groups,
+                size_t* bytes) {
+    if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count < 0");
+    if (count > 0 && !shards) return fail(MUON_ERR_INVALID_ARG, "shards is NULL");
+    *bytes = 0;
+    std::vector<ShardPlan> cur;
+    size_t off = 0;
+    for (int i = 0; i < count; ++i) {
+        const muon_shard& t = shards[i];
+        if (t.rows < 0 || t.cols < 0 || t.full_rows < 0)
+            return fail(MUON_ERR_INVALID_ARG, "negative dimension at index " + std::to_string(i));
+        if (t.cols == 0) continue;
+        if (t.rows > kMaxDim || t.cols > kMaxDim || t.full_rows > kMaxDim || t.rows * t.cols > kMaxElems)
+            return fail(MUON_ERR_TOO_LARGE, "shard " + std::to_string(i) + " too large");
+        if (t.full_rows <= t.cols)
+            return fail(MUON_ERR_INVALID_ARG, "shard " + std::to_string(i) +
+                                                  ": full_rows must exceed cols (flat matrices use rownorm_update)");
+        if (t.rows > t.full_rows)
+            return fail(MUON_ERR_INVALID_ARG, "shard " + std::to_string(i) + ": rows above full_rows");
+        if (cur.size() == size_t(kMaxGroup)) {
+            groups->push_back(std::move(cur));
+            cur.clear();
+            *bytes = std::max(*bytes, off);
+            off = 0;
+        }
+        ShardPlan sp{};
+        sp.idx = i;
+        sp.rows = t.rows;
+        sp.cols = t.cols;
+        sp.chunks = (t.rows + kColChunkRows - 1) / kColChunkRows;
+        sp.partial = off;
+        off += align256(size_t(std::max<int64_t>(sp.chunks, 1)) * size_t(t.cols) * 4);
+        sp.inv = off;
+        off += align256(size_t(t.cols) * 4);
+        cur.push_back(sp);
+    }
+    if (!cur.empty()) {
+        groups->push_back(std::move(cur));
+        *bytes = std::max(*bytes, off);
+    }
+    return MUON_OK;
+}
+
+// Validates pointers, alignment and overlaps of a shard call; `sums` are the caller's
+// per-shard column-sum arrays (written by colsq, read by apply).
+int check_shard_buffers(const muon_shard* shards, const std::vector<std::vector<ShardPlan>>& groups,
+                        const float* const* sums, bool sums_written, bool need_g, size_t need_bytes, void* ws,
+                        size_t ws_bytes, std::vector<Range>& ranges) {
+    if (groups.empty()) return MUON_OK;
+    if (!sums) return fail(MUON_ERR_INVALID_ARG, "column-sum array is NULL");
+    for (const auto& g : groups)
+        for (const ShardPlan& sp : g) {
+            const muon_shard& t = shards[sp.idx];
+            const std::string at = " at index " + std::to_string(sp.idx);
+            const float* cs = sums[sp.idx];
+            if (!cs) return fail(MUON_ERR_INVALID_ARG, "NULL column sums" + at);
+            if (reinterpret_cast<uintptr_t>(cs) & 3) return fail(MUON_ERR_ALIGN, "column sums not 4-byte aligned" + at);
+            const uintptr_t lo = reinterpret_cast<uintptr_t>(cs);
+            ranges.push_back({lo, lo + uintptr_t(sp.cols) * 4, sums_written});
+            if (sp.rows == 0) continue;
+            if (!t.w || !t.m || (need_g && !t.g)) return fail(MUON_ERR_INVALID_ARG, "NULL pointer" + at);
+            if (!aligned16(t.w) || !aligned16(t.m) || (t.g && !aligned16(t.g)))
+                return fail(MUON_ERR_ALIGN, "matrix pointer not 16-byte aligned" + at);
+            const uintptr_t bytes = uintptr_t(sp.rows * sp.cols) * 4;
+            ranges.push_back({reinterpret_cast<uintptr_t>(t.w), reinterpret_cast<uintptr_t>(t.w) + bytes, true});
+            ranges.push_back({reinterpret_cast<uintptr_t>(t.m), reinterpret_cast<uintptr_t>(t.m) + bytes, true});
+            if (need_g)
+                ranges.push_back({reinterpret_cast<uintptr_t>(t.g), reinterpret_cast<uintptr_t>(t.g) + bytes, false});
+        }
+    if (!ws) return fail(MUON_ERR_WORKSPACE, "workspace is NULL");
+    if (ws_bytes < need_bytes)
+        return fail(MUON_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need_bytes) + " bytes");
+    if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(MUON_ERR_ALIGN, "workspace not 256-byte aligned");
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(ws);
+    ranges.push_back({lo, lo + need_bytes, true});
+    return check_overlaps(ranges);
+}
+
 // ------------------------------------------------------ singular spectrum ----
 // SVD-entropy diagnostic ("Muon is Scalable", Sec. 3.4). Per matrix: the fp64 Gram
 // matrix S (m_p x m_p), seven m_p vectors (v_j twice, w, p, d, e, eigenvalues), the
@@ -930,6 +1020,123 @@ MUON_API int adamw_step(const adamw_param* params, int32_t count, const adamw_hp
         blocks += nb;
     }
     return flush();
+}
+
+MUON_API int rownorm_shard_workspace_bytes(const muon_shard* shards, int32_t count, size_t* bytes) {
+    g_last_error.clear();
+    if (!bytes) return fail(MUON_ERR_INVALID_ARG, "bytes is NULL");
+    std::vector<std::vector<ShardPlan>> groups;
+    return plan_shards(shards, count, &groups, bytes);
+}
+
+MUON_API int rownorm_shard_colsq(const muon_shard* shards, int32_t count, const muon_hparams* hp,
+                                 float* const* colsq, void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    int rc = check_hparams(hp, false);
+    if (rc) return rc;
+    std::vector<std::vector<ShardPlan>> groups;
+    size_t need = 0;
+    rc = plan_shards(shards, count, &groups, &need);
+    if (rc) return rc;
+    std::vector<Range> ranges;
+    rc = check_shard_buffers(shards, groups, colsq, true, true, need, workspace, workspace_bytes, ranges);
+    if (rc) return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    for (const auto& g : groups) {
+        ColArgs ca{};
+        ca.mu = hp->mu;
+        ca.eps = hp->eps;
+        ca.sums_only = 1;
+        int64_t tiles = 0, fin = 0;
+        for (const ShardPlan& sp : g) {
+            const muon_shard& t = shards[sp.idx];
+            ColDesc& d = ca.d[ca.n++];
+            d.g = t.g;
+            d.m = t.m;
+            d.partial = reinterpret_cast<float*>(ws + sp.partial);
+            d.inv = colsq[sp.idx];
+            d.rows = int32_t(sp.rows);
+            d.cols = int32_t(sp.cols);
+            d.chunks = int32_t(sp.chunks);  // 0 for an empty block: its sums are written as 0
+            d.tiles_c = int32_t((sp.cols + kColTileCols - 1) / kColTileCols);
+            d.tile_begin = int32_t(tiles);
+            d.fin_begin = int32_t(fin);
+            tiles += int64_t(d.chunks) * d.tiles_c;
+            fin += (sp.cols + 255) / 256;
+        }
+        bool vec = true;
+        for (const ShardPlan& sp : g) vec = vec && (sp.cols % 4 == 0);
+        if (tiles > 0) {
+            ca.total = int32_t(tiles);
+            rc = run_kernel(MUON_KCLASS_COLNORM_PARTIAL, s, "shard colsq partial",
+                            [&] { return launch_colnorm_partial(ca, vec, s); });
+            if (rc) return rc;
+        }
+        rc = run_kernel(MUON_KCLASS_COLNORM_FINALIZE, s, "shard colsq sums",
+                        [&] { return launch_colnorm_finalize(ca, int(fin), s); });
+        if (rc) return rc;
+    }
+    return MUON_OK;
+}
+
+MUON_API int rownorm_shard_apply(const muon_shard* shards, int32_t count, const muon_hparams* hp,
+                                 const float* const* colsq_total, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    g_last_error.clear();
+    int rc = check_hparams(hp, false);
+    if (rc) return rc;
+    std::vector<std::vector<ShardPlan>> groups;
+    size_t need = 0;
+    rc = plan_shards(shards, count, &groups, &need);
+    if (rc) return rc;
+    std::vector<Range> ranges;
+    rc = check_shard_buffers(shards, groups, colsq_total, false, false, need, workspace, workspace_bytes, ranges);
+    if (rc) return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    const float decay = 1.0f - hp->lr * hp->weight_decay;
+    for (const auto& g : groups) {
+        ColArgs fa{}, aa{};  // finalize: totals -> 1 / max(norm, eps); apply: the update
+        fa.eps = aa.eps = hp->eps;
+        fa.decay = aa.decay = decay;
+        int64_t tiles = 0, fin = 0;
+        for (const ShardPlan& sp : g) {
+            const muon_shard& t = shards[sp.idx];
+            ColDesc& f = fa.d[fa.n++];
+            f.partial = const_cast<float*>(colsq_total[sp.idx]);
+            f.inv = reinterpret_cast<float*>(ws + sp.inv);
+            f.cols = int32_t(sp.cols);
+            f.chunks = 1;
+            f.fin_begin = int32_t(fin);
+            fin += (sp.cols + 255) / 256;
+            if (sp.rows == 0) continue;
+            ColDesc& d = aa.d[aa.n++];
+            d.m = t.m;
+            d.w = t.w;
+            d.inv = f.inv;
+            d.rows = int32_t(sp.rows);
+            d.cols = int32_t(sp.cols);
+            d.chunks = int32_t(sp.chunks);
+            d.tiles_c = int32_t((sp.cols + kColTileCols - 1) / kColTileCols);
+            d.tile_begin = int32_t(tiles);
+            // the whole matrix's scale: sqrt(max(A, B)) = sqrt(full_rows) for a tall matrix
+            d.coef = float(double(hp->lr) * double(hp->gamma) * dir_scale(*hp, t.full_rows));
+            tiles += int64_t(d.chunks) * d.tiles_c;
+        }
+        rc = run_kernel(MUON_KCLASS_COLNORM_FINALIZE, s, "shard inverse norms",
+                        [&] { return launch_colnorm_finalize(fa, int(fin), s); });
+        if (rc) return rc;
+        if (aa.n > 0) {
+            bool vec = true;
+            for (int k = 0; k < aa.n; ++k) vec = vec && (aa.d[k].cols % 4 == 0);
+            aa.total = int32_t(tiles);
+            rc = run_kernel(MUON_KCLASS_COLNORM_APPLY, s, "shard apply",
+                            [&] { return launch_colnorm_apply(aa, vec, s); });
+            if (rc) return rc;
+        }
+    }
+    return MUON_OK;
 }
 
 MUON_API int svd_entropy_workspace_bytes(const int64_t* rows, const int64_t* cols, int32_t count,

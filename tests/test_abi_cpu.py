@@ -52,7 +52,7 @@ def test_header_declares_expected_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.muon_abi_version() == 3
+    assert lib.muon_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -343,3 +343,57 @@ def test_svd_entropy_validation(lib):
     rows = (ctypes.c_int64 * 1)(4)
     assert lib.svd_entropy(None, rows, rows, 1, None, 0, None, None, None) == B.MUON_ERR_INVALID_ARG
     assert lib.svd_entropy(None, None, None, -1, None, 0, None, None, None) == B.MUON_ERR_INVALID_ARG
+
+
+# ------------------------------------------------- row-sharded RowNorm share ----
+
+def shard_arr(specs, align=0):
+    """specs: (rows, cols, full_rows); buffers at fake addresses 4 GiB apart."""
+    arr = (B.MuonShard * max(len(specs), 1))()
+    for i, (r, c, a) in enumerate(specs):
+        span = 1 << 32
+        arr[i] = B.MuonShard(r, c, a, BASE + span * (3 * i) + align, BASE + span * (3 * i + 1),
+                             BASE + span * (3 * i + 2))
+    return arr
+
+
+def test_shard_workspace_planning(lib):
+    assert B.rownorm_shard_workspace_bytes([], []) == 0
+    one = B.rownorm_shard_workspace_bytes([(640, 512)], [5120])
+    assert one >= 3 * 512 * 4 + 512 * 4  # three 256-row chunk partials and the inverse norms
+    with pytest.raises(B.MuonError) as e:
+        B.rownorm_shard_workspace_bytes([(640, 512)], [512])  # not tall
+    assert e.value.status == B.MUON_ERR_INVALID_ARG
+    with pytest.raises(B.MuonError) as e:
+        B.rownorm_shard_workspace_bytes([(900, 512)], [800])  # rows above full_rows
+    assert e.value.status == B.MUON_ERR_INVALID_ARG
+    out = ctypes.c_size_t()
+    assert lib.rownorm_shard_workspace_bytes(None, 1, ctypes.byref(out)) == B.MUON_ERR_INVALID_ARG
+
+
+@fake_only
+def test_shard_calls_validation(lib):
+    hp = B.default_hparams()
+    sums = (ctypes.c_void_p * 2)(BASE * 5, BASE * 5 + (1 << 20))
+
+    def colsq(arr, n, ws=BASE * 4, ws_bytes=1 << 34, s=sums, h=hp):
+        return lib.rownorm_shard_colsq(arr, n, ctypes.byref(h) if h is not None else None, s,
+                                       ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+
+    assert colsq(shard_arr([]), 0) == B.MUON_OK
+    assert colsq(shard_arr([(64, 0, 100)]), 1) == B.MUON_OK  # zero columns: skipped
+    assert colsq(shard_arr([(64, 32, 100)]), 1, h=None) == B.MUON_ERR_INVALID_ARG
+    assert colsq(shard_arr([(64, 32, 32)]), 1) == B.MUON_ERR_INVALID_ARG  # not tall
+    assert colsq(shard_arr([(64, 32, 100)], align=8), 1) == B.MUON_ERR_ALIGN
+    assert colsq(shard_arr([(64, 32, 100)]), 1, ws=None) == B.MUON_ERR_WORKSPACE
+    assert colsq(shard_arr([(64, 32, 100)]), 1, ws_bytes=16) == B.MUON_ERR_WORKSPACE
+    bad = (ctypes.c_void_p * 1)(BASE * 5 + 2)
+    assert colsq(shard_arr([(64, 32, 100)]), 1, s=bad) == B.MUON_ERR_ALIGN
+    null = (ctypes.c_void_p * 1)(None)
+    assert colsq(shard_arr([(64, 32, 100)]), 1, s=null) == B.MUON_ERR_INVALID_ARG
+    inside_w = (ctypes.c_void_p * 1)(BASE + 256)  # column sums inside the W block
+    assert colsq(shard_arr([(64, 32, 100)]), 1, s=inside_w) == B.MUON_ERR_ALIAS
+    overlap = (ctypes.c_void_p * 2)(BASE * 5, BASE * 5 + 64)  # two sum arrays overlap
+    assert colsq(shard_arr([(64, 32, 100), (50, 32, 100)]), 2, s=overlap) == B.MUON_ERR_ALIAS
+    assert lib.rownorm_shard_apply(shard_arr([(64, 32, 100)]), 1, ctypes.byref(hp), None,
+                                   ctypes.c_void_p(BASE * 4), 1 << 34, None) == B.MUON_ERR_INVALID_ARG

@@ -1,0 +1,126 @@
+"""GPU parity of one GPU's share of the row-sharded RowNorm step ("Scaling Muon for
+Diffusion Transformers", distributed-implementation paragraph), through the C ABI.
+
+A tall matrix [A, B] split by rows into blocks: rownorm_shard_colsq on every block,
+the column sums added across the blocks (the all-reduce a multi-GPU caller runs; here
+a fixed-order sum of device tensors), then rownorm_shard_apply on every block. The
+concatenated W and M must match the float64 oracle's RowNorm step on the whole matrix
+at the fp32 tolerance (1e-5 relative Frobenius; W also through the W = 0 probe, where
+W' is the update itself), and one block holding the whole matrix must reproduce
+rownorm_update bit for bit (the same sums in the same order).
+Cases: uneven blocks (including an empty block and blocks that are not multiples of
+the 256-row chunk), columns not a multiple of 4, more blocks than one launch group,
+and the hidden-size scale rule.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import muon_oracle as O
+from matrix_orthogonalising_optimizer_02_amd import binding as B
+from matrix_orthogonalising_optimizer_02_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+FP32_TOL = 1e-5
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "the gpu tests need a visible GPU"
+    B.load_library()
+    return torch, torch.device("cuda:0")
+
+
+def rel_fro(x, ref):
+    x, ref = np.asarray(x, np.float64), np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(x - ref) / (den if den > 0 else 1.0))
+
+
+def sharded_step(torch, dev, mats, splits, hp):
+    """mats: list of (w, m_prev, g) host arrays of tall matrices; splits: per matrix the
+    block row counts. Returns the concatenated (W, M) per matrix after the sharded step."""
+    blocks = []  # (matrix index, w, m, g) device blocks
+    for i, ((w, m, g), rows) in enumerate(zip(mats, splits)):
+        assert sum(rows) == w.shape[0]
+        r0 = 0
+        for r in rows:
+            blocks.append((i, *(torch.from_numpy(np.ascontiguousarray(x[r0:r0 + r])).to(dev) for x in (w, m, g))))
+            r0 += r
+    full = [mats[i][0].shape[0] for i, *_ in blocks]
+    colsq = B.rownorm_shard_colsq([b[1] for b in blocks], [b[2] for b in blocks], [b[3] for b in blocks],
+                                  full, hp=hp)
+    totals = []
+    for i in range(len(mats)):  # the all-reduce: blocks of one matrix summed in block order
+        mine = [c for c, b in zip(colsq, blocks) if b[0] == i]
+        t = mine[0].clone()
+        for c in mine[1:]:
+            t += c
+        totals.extend(t.clone() for _ in mine)
+    B.rownorm_shard_apply([b[1] for b in blocks], [b[2] for b in blocks], full, totals, hp=hp)
+    torch.cuda.synchronize()
+    out = []
+    for i in range(len(mats)):
+        ws = [b[1].cpu().numpy() for b in blocks if b[0] == i]
+        ms = [b[2].cpu().numpy() for b in blocks if b[0] == i]
+        out.append((np.concatenate(ws).astype(np.float64), np.concatenate(ms).astype(np.float64)))
+    return out
+
+
+def inputs(key, shapes, w_zero=False):
+    mats = []
+    for i, s in enumerate(shapes):
+        w = np.zeros(s, np.float32) if w_zero else WL.host_normal(key, WL.ROLE_W, i, s, 0.02)
+        mats.append((w, WL.host_normal(key, WL.ROLE_M, i, s, 0.02), WL.host_normal(key, WL.ROLE_G, i, s, 1e-3)))
+    return mats
+
+
+def test_one_block_is_rownorm_update_bitwise(torch_dev):
+    torch, dev = torch_dev
+    hp = B.default_hparams()
+    for shape in [(1000, 300), (1024, 256), (513, 130)]:
+        (w, m, g), = inputs(700, [shape])
+        ref = [torch.from_numpy(x).to(dev) for x in (w, m, g)]
+        B.rownorm_update([ref[0]], [ref[1]], [ref[2]], hp)
+        (ws, ms), = sharded_step(torch, dev, [(w, m, g)], [[shape[0]]], hp)
+        assert np.array_equal(ws, ref[0].cpu().numpy().astype(np.float64)), shape
+        assert np.array_equal(ms, ref[1].cpu().numpy().astype(np.float64)), shape
+
+
+@pytest.mark.parametrize("w_zero", [False, True])
+def test_uneven_blocks_vs_oracle(torch_dev, w_zero):
+    torch, dev = torch_dev
+    hp = B.default_hparams()
+    ohp = O.OracleHParams()
+    shapes = [(2000, 384), (777, 130)]
+    splits = [[300, 256, 0, 513, 1, 250, 380, 300], [100, 77, 300, 300]]
+    mats = inputs(701, shapes, w_zero)
+    got = sharded_step(torch, dev, mats, splits, hp)
+    for s, (w, m, g), (ws, ms) in zip(shapes, mats, got):
+        w_ref, m_ref = O.rownorm_step(w, m, g, ohp)
+        em, ew = rel_fro(ms, m_ref), rel_fro(ws, w_ref)
+        log(f"{s} in {len(splits[shapes.index(s)])} blocks, W = 0: {w_zero}: M err {em:.2e}, W err {ew:.2e}")
+        assert em < FP32_TOL and ew < FP32_TOL, (s, em, ew)
+
+
+def test_two_groups_and_hidden_scale(torch_dev):
+    torch, dev = torch_dev
+    hp = B.default_hparams(scale_mode=B.SCALE_HIDDEN, hidden=512)
+    ohp = O.OracleHParams(scale_mode="hidden", hidden=512)
+    shapes = [(1200, 256), (900, 300), (640, 96)]
+    splits = [[150] * 8, [100] * 9, [160, 160, 160, 160]]  # 21 blocks: two launch groups
+    mats = inputs(702, shapes, w_zero=True)
+    got = sharded_step(torch, dev, mats, splits, hp)
+    for s, (w, m, g), (ws, ms) in zip(shapes, mats, got):
+        w_ref, m_ref = O.rownorm_step(w, m, g, ohp)
+        em, ew = rel_fro(ms, m_ref), rel_fro(ws, w_ref)
+        log(f"{s}, hidden-size scale: M err {em:.2e}, update err {ew:.2e}")
+        assert em < FP32_TOL and ew < FP32_TOL, (s, em, ew)
