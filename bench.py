@@ -96,6 +96,8 @@ def parse():
                     help="timed SVD-entropy diagnostic calls over the layer set (0 = skip)")
     ap.add_argument("--shard-degree", type=int, default=8,
                     help="time one GPU's share of the row-sharded RowNorm step at this degree (0 = skip)")
+    ap.add_argument("--graph-cycles", type=int, default=20,
+                    help="eager vs HIP-graph-replayed Periodic cycles on the small workloads (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
@@ -195,6 +197,16 @@ def measure_variants(pkg, torch, weights, momenta, grads, ws, k, wl, n, say):
     res["unmonitored_rownorm_step_ms"] = round(timed(
         lambda: pkg.muon_step(weights, momenta, grads[1], 1, hp, ws)), 4)
     res["update_rms_last"] = [round(float(x), 5) for x in rms.cpu().tolist()]
+    # ns5_batched: O = NS5(M) for the set into separate fp32 outputs (the entry point
+    # without momentum or update), NS5 TFLOP/s on the symmetric count
+    outs = [torch.empty_like(m) for m in momenta]
+    hp_ns = pkg.default_hparams()
+    pkg.ns5_batched(momenta, outs, hp_ns, ws)
+    t = timed(lambda: pkg.ns5_batched(momenta, outs, hp_ns, ws))
+    flops = sum(ns5_flops_sym(min(s), max(s), hp_ns.ns_steps) for s in shapes)
+    res["ns5_batched_ms"] = round(t, 4)
+    res["ns5_batched_tflops"] = round(flops / (t * 1e-3) / 1e12, 1)
+    del outs
     say(f"variants: {res}")
     return res
 
@@ -373,6 +385,56 @@ def measure_shard_rownorm(pkg, torch, dev, wl, degree, reps, rn_ms, say):
     return res
 
 
+def measure_graph(pkg, torch, dev, n, say):
+    """Eager Periodic cycles against the same cycle captured once in a HIP graph and
+    replayed, on the small workloads where launches dominate (the 128 x 512 matrix and
+    the H = 2048 DiT block). Inputs resident; HIP events around n cycles."""
+    from matrix_orthogonalising_optimizer_02_amd import workloads as WL
+
+    res = {}
+    for wl in (WL.SINGLE_128x512, WL.DIT_BLOCK_H2048):
+        shapes = list(wl.shapes)
+        w = [torch.empty(s, dtype=torch.float32, device=dev) for s in shapes]
+        m = [torch.zeros(s, dtype=torch.float32, device=dev) for s in shapes]
+        g = [[torch.empty(s, dtype=torch.float32, device=dev) for s in shapes] for _ in range(3)]
+        for i, t in enumerate(w):
+            WL.device_fill(t, wl.key, WL.ROLE_W, i, wl.w_std)
+        for j in range(3):
+            for i, t in enumerate(g[j]):
+                WL.device_fill(t, wl.key, WL.ROLE_G, i, wl.g_std, wl.g_dist, j)
+        ws = pkg.make_workspace(shapes, dev)
+        hp = pkg.default_hparams(period_k=3)
+
+        def cycle():
+            for j in range(3):
+                pkg.muon_step(w, m, g[j], j, hp, ws)
+
+        def timed(fn):
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(n):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / n
+
+        eager = timed(cycle)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            cycle()
+        replay = timed(graph.replay)
+        res[wl.name] = {"eager_cycle_ms": round(eager, 4), "graph_cycle_ms": round(replay, 4),
+                        "speedup": round(eager / replay, 3)}
+        del graph, w, m, g, ws
+    say(f"graph: {res}")
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -468,6 +530,7 @@ def main():
     rn_gbs = 20.0 * wl.elements / (rn_ms * 1e-3) / 1e9
     shard = measure_shard_rownorm(pkg, torch, dev, wl, args.shard_degree, 10, rn_ms, say) \
         if args.shard_degree > 1 else None
+    graph = measure_graph(pkg, torch, dev, args.graph_cycles, say) if args.graph_cycles > 0 else None
     # dominant kernel: the B X product of iterations 1..N-1
     apply_launch_ms = ms["apply"] / max(cnt["apply"], 1)
     apply_launch_flops = sum(apply_flops(min(s), max(s)) for s in shapes)
@@ -546,6 +609,8 @@ def main():
         out["spectrum"] = spectrum
     if shard is not None:
         out["shard_rownorm"] = shard
+    if graph is not None:
+        out["graph_replay"] = graph
     if not args.no_cpu_baseline:
         say("cpu baseline: timing the float64 oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(wl, k)
