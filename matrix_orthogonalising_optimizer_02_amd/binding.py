@@ -380,6 +380,8 @@ def _shard_ws(workspace, weights, full_rows, dev):
 
 def _sum_ptrs(tensors, weights, name):
     torch = _torch()
+    if len(tensors) != len(weights):
+        raise ValueError(f"{name} needs one column-sum tensor per block")
     ptrs = (ctypes.c_void_p * max(len(weights), 1))()
     for i, (t, w) in enumerate(zip(tensors, weights)):
         if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 1 \
