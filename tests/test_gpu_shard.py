@@ -124,3 +124,27 @@ def test_two_groups_and_hidden_scale(torch_dev):
         em, ew = rel_fro(ms, m_ref), rel_fro(ws, w_ref)
         log(f"{s}, hidden-size scale: M err {em:.2e}, update err {ew:.2e}")
         assert em < FP32_TOL and ew < FP32_TOL, (s, em, ew)
+
+
+@pytest.mark.parametrize("seed", list(range(4)))
+def test_random_blocks(torch_dev, seed):
+    """Seeded random tall matrices cut into 1-9 random blocks (empty blocks allowed)."""
+    torch, dev = torch_dev
+    rng = np.random.default_rng(710 + seed)
+    shapes = []
+    for _ in range(int(rng.integers(1, 4))):
+        b = int(rng.integers(1, 400))
+        shapes.append((b + int(rng.integers(1, 1200)), b))
+    splits = []
+    for a, _ in shapes:
+        cuts = np.sort(rng.integers(0, a + 1, size=int(rng.integers(0, 9))))
+        edges = [0, *cuts.tolist(), a]
+        splits.append([edges[i + 1] - edges[i] for i in range(len(edges) - 1)])
+    mats = inputs(720 + seed, shapes, w_zero=bool(seed % 2))
+    hp = B.default_hparams()
+    got = sharded_step(torch, dev, mats, splits, hp)
+    for s, (w, m, g), (ws, ms) in zip(shapes, mats, got):
+        w_ref, m_ref = O.rownorm_step(w, m, g, O.OracleHParams())
+        em, ew = rel_fro(ms, m_ref), rel_fro(ws, w_ref)
+        assert em < FP32_TOL and ew < FP32_TOL, (seed, s, em, ew)
+    log(f"seed {seed}: {len(shapes)} matrices {shapes}, blocks {splits}: ok")

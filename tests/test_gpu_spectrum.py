@@ -190,3 +190,16 @@ def test_nan_and_inf_propagate_per_matrix(torch_dev):
     # no finite sigma^2 survives (NaN, or Inf where the Gershgorin bound is infinite)
     assert not np.any(np.isfinite(sig[150:150 + 90])) and not np.any(np.isfinite(sig[240:240 + 64]))
     check([good], ent[:1], sig[:150], label="beside NaN / Inf matrices")
+
+
+@pytest.mark.parametrize("seed", list(range(4)))
+def test_random_sets(torch_dev, seed):
+    """Seeded random sets: 1-20 matrices (so sometimes two launch groups), each side 1-500."""
+    torch, dev = torch_dev
+    rng = np.random.default_rng(620 + seed)
+    count = int(rng.integers(1, 21))
+    shapes = [(int(rng.integers(1, 501)), int(rng.integers(1, 501))) for _ in range(count)]
+    mats = [WL.host_normal(630 + seed, WL.ROLE_W, i, s, float(10.0 ** rng.uniform(-3, 1)))
+            for i, s in enumerate(shapes)]
+    ent, sig = run(torch, dev, mats)
+    check(mats, ent, sig, label=f"random seed {seed}, {count} matrices")
