@@ -96,6 +96,8 @@ def parse():
                     help="timed SVD-entropy diagnostic calls over the layer set (0 = skip)")
     ap.add_argument("--shard-degree", type=int, default=8,
                     help="time one GPU's share of the row-sharded RowNorm step at this degree (0 = skip)")
+    ap.add_argument("--ns5-batched", type=int, default=1,
+                    help="also time ns5_batched over the set in the variants leg (0 = skip)")
     ap.add_argument("--graph-cycles", type=int, default=20,
                     help="eager vs HIP-graph-replayed Periodic cycles on the small workloads (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -155,7 +157,7 @@ def cpu_baseline(wl, k):
             "vanilla_step_ms": round(1e3 * ref_total, 1), "rownorm_step_ms": round(1e3 * rn_total, 1)}
 
 
-def measure_variants(pkg, torch, weights, momenta, grads, ws, k, wl, n, say):
+def measure_variants(pkg, torch, weights, momenta, grads, ws, k, wl, n, say, ns5_calls=1):
     """Refresh steps under the Eq. 5 and Eq. 6 scale rules and a Periodic cycle with the
     update-RMS monitor, on the same resident state (HIP events around each block)."""
     shapes = [tuple(w.shape) for w in weights]
@@ -199,14 +201,15 @@ def measure_variants(pkg, torch, weights, momenta, grads, ws, k, wl, n, say):
     res["update_rms_last"] = [round(float(x), 5) for x in rms.cpu().tolist()]
     # ns5_batched: O = NS5(M) for the set into separate fp32 outputs (the entry point
     # without momentum or update), NS5 TFLOP/s on the symmetric count
-    outs = [torch.empty_like(m) for m in momenta]
-    hp_ns = pkg.default_hparams()
-    pkg.ns5_batched(momenta, outs, hp_ns, ws)
-    t = timed(lambda: pkg.ns5_batched(momenta, outs, hp_ns, ws))
-    flops = sum(ns5_flops_sym(min(s), max(s), hp_ns.ns_steps) for s in shapes)
-    res["ns5_batched_ms"] = round(t, 4)
-    res["ns5_batched_tflops"] = round(flops / (t * 1e-3) / 1e12, 1)
-    del outs
+    if ns5_calls > 0:
+        outs = [torch.empty_like(m) for m in momenta]
+        hp_ns = pkg.default_hparams()
+        pkg.ns5_batched(momenta, outs, hp_ns, ws)
+        t = timed(lambda: pkg.ns5_batched(momenta, outs, hp_ns, ws))
+        flops = sum(ns5_flops_sym(min(s), max(s), hp_ns.ns_steps) for s in shapes)
+        res["ns5_batched_ms"] = round(t, 4)
+        res["ns5_batched_tflops"] = round(flops / (t * 1e-3) / 1e12, 1)
+        del outs
     say(f"variants: {res}")
     return res
 
@@ -513,7 +516,8 @@ def main():
     vanilla_ms = ev2.elapsed_time(ev3) / max(args.vanilla_steps, 1)
     say(f"vanilla: {vanilla_ms:.3f} ms per step")
 
-    variants = measure_variants(pkg, torch, weights, momenta, grads, ws, k, wl, args.variant_steps, say) \
+    variants = measure_variants(pkg, torch, weights, momenta, grads, ws, k, wl, args.variant_steps, say,
+                                args.ns5_batched) \
         if args.variant_steps > 0 else None
     hybrid = measure_adamw(pkg, torch, dev, wl, args.adamw_steps, say) if args.adamw_steps > 0 else None
     spectrum = measure_spectrum(pkg, torch, weights, args.spectrum_calls, say, not args.no_cpu_baseline) \
