@@ -72,13 +72,71 @@ def measured_traffic(kernel, workload_key):
     with open(path) as fh:
         rec = json.load(fh)
     h = hashlib.sha256()
-    for src in rec["gemm_sources"]:
+    for src in GEMM_SOURCES:
         with open(os.path.join(ROOT, "matrix_orthogonalising_optimizer_02_amd", "csrc", src), "rb") as fh:
             h.update(fh.read())
     if h.hexdigest() != rec["gemm_source_sha256"]:
         return None
     entry = rec["kernels"].get(kernel)
     return None if entry is None else entry["hbm_bytes_per_dispatch"]
+
+
+GEMM_SOURCES = ["gemm_kernel.hpp", "k_gemm.hip", "launch.hpp", "common.hpp"]
+
+
+def summarize_traffic(cal_fetch, cal_write, run_fetch, run_write, out):
+    """Write the per-dispatch HBM traffic record that measured_traffic() reads.
+
+    Inputs are rocprofv3 --pmc counter CSVs (run_counter_collection.csv): FETCH_SIZE and
+    WRITE_SIZE of a calibration run (a torch copy of 2^28 fp32, 1 GiB read and 1 GiB
+    written, dispatched as __amd_rocclr_copyBuffer) and of a benchmark run, each counter
+    from its own run. Bytes = counter KiB x 1024 x the copy's calibration factor, averaged
+    over each kernel's dispatches. The record carries the hash of the GEMM sources.
+    """
+    import collections
+    import csv
+    import hashlib
+
+    def per_kernel(path, counter):
+        per_dispatch, names = collections.defaultdict(float), {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                per_dispatch[r["Dispatch_Id"]] += float(r["Counter_Value"])
+                names[r["Dispatch_Id"]] = r["Kernel_Name"]
+        agg = collections.defaultdict(list)
+        for d, v in per_dispatch.items():
+            n = names[d]
+            if "muon::" not in n and "rocclr_copyBuffer" not in n:
+                continue
+            short = n.replace("void ", "").split("(")[0]
+            agg[short[len("muon::"):] if short.startswith("muon::") else short].append(v)
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+
+    cf, cw = per_kernel(cal_fetch, "FETCH_SIZE"), per_kernel(cal_write, "WRITE_SIZE")
+    ck = [k for k in cf if "copyBuffer" in k][0]
+    gib_kib = 1024.0 * 1024.0
+    ff, wf = gib_kib / cf[ck], gib_kib / cw[ck]
+    bf, bw = per_kernel(run_fetch, "FETCH_SIZE"), per_kernel(run_write, "WRITE_SIZE")
+    h = hashlib.sha256()
+    for src in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "matrix_orthogonalising_optimizer_02_amd", "csrc", src), "rb") as fh:
+            h.update(fh.read())
+    rec = {"workload": "15B-scale layer set H=5120 (10 matrices)",
+           "calibration": {"kernel": "__amd_rocclr_copyBuffer (torch copy_ of 2^28 fp32 = 1 GiB read + 1 GiB written)",
+                           "fetch_kib": cf[ck], "write_kib": cw[ck], "fetch_factor": round(ff, 4),
+                           "write_factor": round(wf, 4)},
+           "gemm_source_sha256": h.hexdigest(), "gemm_sources": GEMM_SOURCES, "kernels": {}}
+    for k in sorted(set(bf) | set(bw)):
+        if "copyBuffer" in k:
+            continue
+        f, w = bf.get(k, 0.0), bw.get(k, 0.0)
+        rec["kernels"][k] = {"fetch_kib_per_dispatch": round(f), "write_kib_per_dispatch": round(w),
+                             "hbm_bytes_per_dispatch": round((f * ff + w * wf) * 1024)}
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return rec
 
 
 def parse():
@@ -101,6 +159,8 @@ def parse():
     ap.add_argument("--graph-cycles", type=int, default=20,
                     help="eager vs HIP-graph-replayed Periodic cycles on the small workloads (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-traffic", nargs=5, metavar=("CAL_FETCH", "CAL_WRITE", "RUN_FETCH", "RUN_WRITE", "OUT"),
+                    help="write the HBM traffic record from rocprofv3 counter CSVs and exit (no GPU)")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -440,6 +500,10 @@ def measure_graph(pkg, torch, dev, n, say):
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        rec = summarize_traffic(*args.summarize_traffic)
+        print(json.dumps({k: v["hbm_bytes_per_dispatch"] for k, v in rec["kernels"].items()}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "
               "(one GPU's share of the sharded step is what it measures)", file=sys.stderr)
