@@ -326,3 +326,18 @@ def test_pins_reject_planted_rownorm_and_update_mistakes():
     bad = -HP.lr * 0.2 * 25 * svd_closed_form(HP.mu * mp + g)
     w1, _ = O.muon_step(np.zeros((10, 25)), mp, g, 0, HP)
     assert rel_fro(w1, good) < 1e-10 and rel_fro(bad, good) > 1.0
+
+
+@pytest.mark.parametrize("steps", [1, 2, 3, 10])
+def test_ns_other_iteration_counts_equal_svd_closed_form(steps):
+    """The iteration count is a parameter ([MS] Sec. 2.2 sets N = 5; N = 10 is a listed
+    variant): N iterations give U f^N(Sigma / ||M||_F) V^T for any N, flat and tall."""
+    rng = np.random.default_rng(70 + steps)
+    for shape in [(12, 40), (40, 12)]:
+        m = rng.normal(size=shape)
+        assert rel_fro(O.newton_schulz(m, steps=steps), svd_closed_form(m, steps)) < 1e-10
+    # one iteration from a rank-one input: f(1) = a + b + c exactly
+    u, v = rng.normal(size=7), rng.normal(size=9)
+    o = O.newton_schulz(np.outer(u, v), steps=1)
+    expect = (HP.ns_a + HP.ns_b + HP.ns_c) * np.outer(u / np.linalg.norm(u), v / np.linalg.norm(v))
+    assert np.max(np.abs(o - expect)) < 1e-13
