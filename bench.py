@@ -211,6 +211,7 @@ def cpu_baseline(wl, k):
     rn_total = t_rn * wl.elements / (shape[0] * shape[1])
     avg_ms = 1e3 * (ref_total + (k - 1) * rn_total) / k
     return {"value": round(avg_ms, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
+            "host": host_info(),
             "sample": f"oracle refresh step ({t_ref:.1f} s) and RowNorm step ({t_rn:.2f} s), medians of "
                       f"{reps} runs on the {shape[0]}x{shape[1]} matrix, scaled by flops and elements to the "
                       f"{len(wl.shapes)}-matrix set; value = mean ms per optimizer step over a K={k} cycle",
@@ -387,6 +388,27 @@ def spectrum_oracle_time(weights, shapes):
             "sample": f"oracle SVD entropy of the {shapes[idx][0]}x{shapes[idx][1]} matrix, scaled by "
                       f"4 m^2 n - 4 m^3 / 3 to the {len(shapes)}-matrix set",
             "cores": _blas_threads()}
+
+
+def host_info():
+    """CPU model and BLAS library of the host the oracle ran on."""
+    info = {"cpu": None, "blas": None}
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    info["cpu"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        if libs:
+            info["blas"] = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:
+        pass
+    return info
 
 
 def _blas_threads():
