@@ -22,13 +22,12 @@ from oracle import muon_oracle as O
 from matrix_orthogonalising_optimizer_02_amd import binding as B
 from matrix_orthogonalising_optimizer_02_amd import hybrid as H
 from matrix_orthogonalising_optimizer_02_amd import workloads as WL
+from tolerances import FP32_TOL, NS_TOL
 
 pytestmark = pytest.mark.gpu
 
 UPD_TOL = 1e-5
 MOM_TOL = 1e-6
-NS_TOL = 2e-2
-FP32_TOL = 1e-5
 # The device receives fp32 hyperparameters; the oracle gets the same values (1 - beta2
 # would otherwise amplify the fp32 rounding of 0.999 a thousandfold, to 1.3e-5).
 AHP = A.AdamWHParams(**{f: float(np.float32(getattr(A.AdamWHParams(), f)))

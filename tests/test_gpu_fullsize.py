@@ -24,11 +24,10 @@ import pytest
 from oracle import muon_oracle as O
 from matrix_orthogonalising_optimizer_02_amd import binding as B
 from matrix_orthogonalising_optimizer_02_amd import workloads as WL
+from tolerances import FP32_TOL, NS_TOL
 
 pytestmark = pytest.mark.gpu
 
-NS_TOL = 2e-2
-FP32_TOL = 1e-5
 HP = O.OracleHParams()
 
 

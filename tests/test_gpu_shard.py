@@ -20,10 +20,9 @@ import pytest
 from oracle import muon_oracle as O
 from matrix_orthogonalising_optimizer_02_amd import binding as B
 from matrix_orthogonalising_optimizer_02_amd import workloads as WL
+from tolerances import FP32_TOL
 
 pytestmark = pytest.mark.gpu
-
-FP32_TOL = 1e-5
 
 
 def log(msg):
