@@ -158,6 +158,8 @@ def parse():
                     help="also time ns5_batched over the set in the variants leg (0 = skip)")
     ap.add_argument("--graph-cycles", type=int, default=20,
                     help="eager vs HIP-graph-replayed Periodic cycles on the small workloads (0 = skip)")
+    ap.add_argument("--config-cycles", type=int, default=10,
+                    help="timed Periodic cycles (and vanilla steps) on each other multi-matrix workload (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-traffic", nargs=5, metavar=("CAL_FETCH", "CAL_WRITE", "RUN_FETCH", "RUN_WRITE", "OUT"),
                     help="write the HBM traffic record from rocprofv3 counter CSVs and exit (no GPU)")
@@ -272,6 +274,71 @@ def measure_variants(pkg, torch, weights, momenta, grads, ws, k, wl, n, say, ns5
         res["ns5_batched_tflops"] = round(flops / (t * 1e-3) / 1e12, 1)
         del outs
     say(f"variants: {res}")
+    return res
+
+
+def measure_configs(pkg, torch, dev, names, cycles, say):
+    """The step figures for the other multi-matrix workloads, in the same run: Periodic
+    (K = 3) and vanilla step times, NS5 TFLOP/s and RowNorm GB/s with their roofline
+    fractions, from the library's per-launch HIP events. State is freed after each."""
+    from matrix_orthogonalising_optimizer_02_amd import workloads as WL
+    k = 3
+    res = {}
+    for name in names:
+        wl = pick_workload(name)
+        shapes = list(wl.shapes)
+        weights = [torch.empty(s, dtype=torch.float32, device=dev) for s in shapes]
+        momenta = [torch.zeros(s, dtype=torch.float32, device=dev) for s in shapes]
+        for i, w in enumerate(weights):
+            WL.device_fill(w, wl.key, WL.ROLE_W, i, wl.w_std)
+        grads = []
+        for step in range(k):
+            gs = [torch.empty(s, dtype=torch.float32, device=dev) for s in shapes]
+            for i, g in enumerate(gs):
+                WL.device_fill(g, wl.key, WL.ROLE_G, i, wl.g_std, wl.g_dist, step)
+            grads.append(gs)
+        ws = pkg.make_workspace(shapes, dev)
+        hp = pkg.default_hparams(period_k=k)
+        hp1 = pkg.default_hparams(period_k=1)
+        for s in range(2 * k):  # warm-up: two cycles
+            pkg.muon_step(weights, momenta, grads[s % k], s, hp, ws)
+        torch.cuda.synchronize()
+        pkg.timing_enable(True)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for s in range(cycles * k):
+            pkg.muon_step(weights, momenta, grads[s % k], s, hp, ws)
+        b.record()
+        torch.cuda.synchronize()
+        kern = pkg.timing_read()
+        pkg.timing_enable(False)
+        periodic_ms = a.elapsed_time(b) / (cycles * k)
+        a.record()
+        for s in range(cycles):
+            pkg.muon_step(weights, momenta, grads[s % k], 0, hp1, ws)
+        b.record()
+        torch.cuda.synchronize()
+        vanilla_ms = a.elapsed_time(b) / cycles
+        ms = {n_: kern[n_][0] for n_ in kern}
+        ns5_ms = (ms["gram"] + ms["poly"] + ms["apply"] + ms["apply_final"]) / cycles
+        ns5_tf = sum(ns5_flops_sym(min(s), max(s), hp.ns_steps) for s in shapes) / (ns5_ms * 1e-3) / 1e12
+        rn_ms = (ms["rownorm_rows"] + ms["colnorm_partial"] + ms["colnorm_finalize"]
+                 + ms["colnorm_apply"]) / (cycles * (k - 1))
+        rn_gbs = 20.0 * wl.elements / (rn_ms * 1e-3) / 1e9
+        ap_ms = ms["apply"] / max(kern["apply"][1], 1)
+        ap_tf = sum(apply_flops(min(s), max(s)) for s in shapes) / (ap_ms * 1e-3) / 1e12
+        res[name] = {"workload": wl.name, "matrices": len(shapes), "elements": wl.elements,
+                     "muon_step_ms_periodic_avg": round(periodic_ms, 4),
+                     "muon_step_ms_vanilla": round(vanilla_ms, 4),
+                     "periodic_saving_pct": round(100.0 * (1.0 - periodic_ms / vanilla_ms), 1),
+                     "ns5_ms_per_refresh": round(ns5_ms, 4), "ns5_tflops": round(ns5_tf, 1),
+                     "ns5_frac_of_bf16_peak": round(ns5_tf / PEAK_BF16_TFLOPS, 4),
+                     "apply_tflops": round(ap_tf, 1),
+                     "rownorm_step_ms": round(rn_ms, 4), "rownorm_gbs": round(rn_gbs, 1),
+                     "rownorm_frac_of_hbm_peak": round(rn_gbs / PEAK_HBM_GBS, 4)}
+        say(f"config {name}: {res[name]}")
+        del weights, momenta, grads, ws
+        torch.cuda.empty_cache()
     return res
 
 
@@ -621,6 +688,8 @@ def main():
     shard = measure_shard_rownorm(pkg, torch, dev, wl, args.shard_degree, 10, rn_ms, say) \
         if args.shard_degree > 1 else None
     graph = measure_graph(pkg, torch, dev, args.graph_cycles, say) if args.graph_cycles > 0 else None
+    others = [w for w in ("dit2048", "bucket2048", "mmdit3072", "15b") if w != args.workload]
+    configs = measure_configs(pkg, torch, dev, others, args.config_cycles, say) if args.config_cycles > 0 else None
     # dominant kernel: the B X product of iterations 1..N-1
     apply_launch_ms = ms["apply"] / max(cnt["apply"], 1)
     apply_launch_flops = sum(apply_flops(min(s), max(s)) for s in shapes)
@@ -701,6 +770,8 @@ def main():
         out["shard_rownorm"] = shard
     if graph is not None:
         out["graph_replay"] = graph
+    if configs is not None:
+        out["configs"] = configs
     if not args.no_cpu_baseline:
         say("cpu baseline: timing the float64 oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(wl, k)
