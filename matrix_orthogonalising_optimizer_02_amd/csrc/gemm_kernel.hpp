@@ -166,10 +166,29 @@ __device__ __forceinline__ void tri_tile(int local, int T, int& ti, int& tj) {
     ti = tj = 0;  // not reached for local < T (T + 1) / 2
 }
 
+// Slot `sl` of XCD x -> (matrix gi, tile index local): every XCD walks the group's
+// matrices in order and takes one contiguous eighth of each one's tiles. gi = -1 when
+// the XCD has fewer slots.
+__device__ __forceinline__ void xcd_slot(const NsArgs& args, int x, int sl, int& gi, int& local) {
+    gi = -1;
+    for (int g = 0; g < args.n; ++g) {
+        const int T = args.d[g].ntiles;
+        const int lo = (x * T) >> 3, cnt = (((x + 1) * T) >> 3) - lo;
+        if (sl < cnt) {
+            gi = g;
+            local = lo + sl;
+            return;
+        }
+        sl -= cnt;
+    }
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
 
-template <int MODE, class Cfg>
+// kSplitOK: the instance used by launches that split their tail tiles (the others
+// compile without the chunk logic).
+template <int MODE, class Cfg, bool kSplitOK = false>
 __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short* smem) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NT = Cfg::NT;
     constexpr int WM = Cfg::WM, WN = Cfg::WN, TM = Cfg::TM, TN = Cfg::TN;
@@ -189,25 +208,30 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
     // eighth of each matrix's tile sequence: equal work per XCD even when the matrices'
     // K differ, and neighbouring tiles (shared operand panels) in the same L2. Blocks
     // left without a tile (the grid is 8 x the largest per-XCD count) exit here.
+    constexpr bool kSym = (MODE == kModeGram || MODE == kModePoly);
+    // Tail split (symmetric stages on the direct-load tile): the XCD's blocks from
+    // xfull[x] on are chunk c of its tail tile xfull[x] + u / S, u = block - xfull[x].
+    constexpr bool kSplit = kSym && Cfg::kDirect && kSplitOK;
+    int chunk = -1, nsplit = 1, unit = 0;
     int gi = -1, local = 0;
     {
         const int x = blockIdx.x & 7;
         int sl = blockIdx.x >> 3;
-        for (int g = 0; g < args.n; ++g) {
-            const int T = args.d[g].ntiles;
-            const int lo = (x * T) >> 3, cnt = (((x + 1) * T) >> 3) - lo;
-            if (sl < cnt) {
-                gi = g;
-                local = lo + sl;
-                break;
+        if constexpr (kSplit) {
+            if (sl >= args.xfull[x]) {
+                const int u = sl - args.xfull[x];
+                nsplit = args.xsplit[x];
+                if (u >= args.xtail[x] * nsplit) return;
+                chunk = u % nsplit;
+                sl = args.xfull[x] + u / nsplit;
+                unit = args.xpbase[x] + u;
             }
-            sl -= cnt;
         }
+        xcd_slot(args, x, sl, gi, local);
     }
     if (gi < 0) return;
     const NsDesc& d = args.d[gi];
 
-    constexpr bool kSym = (MODE == kModeGram || MODE == kModePoly);
     int ti, tj;
     if constexpr (kSym) tri_tile(local, d.tiles, ti, tj);
     else rect_tile(local, d.m_p / BM, d.tiles, ti, tj);
@@ -245,7 +269,21 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    const int nk = K / BK;
+    // K steps of this block: all of K, or chunk c of nsplit, cut at multiples of 256 (K
+    // is one): the chunk's start is then a fixed offset of the tile's operand pointers
+    // in both the K-major and the K-contiguous panel layouts.
+    int nk = K / BK;
+    if (chunk >= 0) {
+        const int n256 = K >> 8;
+        const int c0 = (chunk * n256) / nsplit, c1 = ((chunk + 1) * n256) / nsplit;
+        nk = (c1 - c0) * (256 / BK);
+        const int64_t kofs = kTr ? (((int64_t)c0 * (ld >> 5)) << 13) : ((int64_t)(c0 * 8) << 13);
+        Pt += kofs;
+        Qt += kofs;
+    }
+    // partial tile of unit u, this wave's accumulators in register order (256-byte rows)
+    float* const tail_w = kSplit ? args.tail + (int64_t)unit * kTailUnitFloats + wave * (TM * TN * 16 * 64) + lane
+                                 : nullptr;
 
     if constexpr (Cfg::kDirect) {
         // 1 KiB load j covers rows RPI*j .. RPI*j + RPI-1: lane l lands on row
@@ -417,6 +455,17 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         for (; kt + 1 < nk; ++kt) kstep(kt, BoolC<false>{}, BoolC<true>{});
         if (kt < nk) kstep(kt, BoolC<false>{}, BoolC<false>{});
         __syncthreads();
+        if constexpr (kSplit) {
+            if (chunk >= 0) {  // a tail chunk: partial sums out, the fixup finishes the tile
+#pragma unroll
+                for (int a = 0; a < TM; ++a)
+#pragma unroll
+                    for (int b = 0; b < TN; ++b)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) tail_w[((a * TN + b) * 16 + r) * 64] = acc[a][b][r];
+                return;
+            }
+        }
     } else {
         // element (row, k) of the P / Q tile: blocked work matrices or the row-major X_r
         auto pa = [&](int row, int k) -> const unsigned short* {

@@ -74,13 +74,28 @@ struct NsDesc {
     float* part;           // final modes, optional: [ntiles * 4] per-wave sums of O^2
 };
 
+// Symmetric stages on big tiles may split the last round of tiles of an XCD: its
+// sequence of tiles ends with xtail[x] tiles that run as xsplit[x] chunks of K each
+// (blocks xfull[x] .. xfull[x] + xtail[x] * xsplit[x] - 1 of the XCD), writing fp32
+// partial tiles (kTailUnitFloats each, accumulator order) at tail + (xpbase[x] + u) *
+// kTailUnitFloats. A fixup launch of sum(xtail) blocks adds each tile's chunks in chunk
+// order and runs the stage's epilogue. tail == nullptr: no split.
+#ifndef MUON_GEMM_TAIL_SPLIT
+#define MUON_GEMM_TAIL_SPLIT 1
+#endif
+constexpr bool kGemmTailSplit = MUON_GEMM_TAIL_SPLIT != 0;
+constexpr int kTailUnitFloats = 256 * 256;
+constexpr int kTailMaxSplit = 8;
 struct NsArgs {
     NsDesc d[kMaxGroup];
     int32_t n;
-    int32_t total;         // grid size: 8 x the largest per-XCD tile count
+    int32_t total;         // grid size: 8 x the largest per-XCD block count
     float ca, cb, cc;
     float decay;           // 1 - lr * weight_decay
     int32_t first;         // first iteration: fold s into the epilogues
+    float* tail;
+    int32_t xfull[8], xtail[8], xsplit[8], xpbase[8];
+    int32_t fix_total;     // blocks of the fixup launch
 };
 
 // ---- RowNorm step ---------------------------------------------------------------

@@ -68,7 +68,64 @@ struct MatPlan {
 struct GroupPlan {
     std::vector<MatPlan> mats;
     size_t bytes = 0;
+    size_t tail = 0;          // fp32 partial tiles of the split symmetric stages
+    int64_t tail_units = 0;
 };
+
+// MI355X: 256 compute units in 8 XCDs; a big-tile block fills one compute unit.
+constexpr int kCusPerXcd = 32;
+
+// Tail split of a symmetric stage on big tiles. XCD x runs cnt[x] tiles in rounds of
+// kCusPerXcd blocks; a last round of r <= kCusPerXcd / 2 tiles would leave most of the
+// XCD idle while it runs, so those r tiles run as S chunks of K each (S r <= kCusPerXcd,
+// S <= kTailMaxSplit, chunks cut at multiples of 256 of K, i.e. of 8 K steps). Returns
+// the number of partial tiles (0: no split).
+int64_t tail_split(const int64_t cnt[8], int64_t min_ksteps, NsArgs* na) {
+    int64_t units = 0;
+    for (int x = 0; x < 8; ++x) {
+        const int64_t r = cnt[x] % kCusPerXcd;
+        int64_t S = 1;
+        if (r > 0 && r <= kCusPerXcd / 2)
+            S = std::min<int64_t>({kTailMaxSplit, kCusPerXcd / r, min_ksteps / 8});
+        if (S < 2) S = 1;
+        const int64_t tail = S > 1 ? r : 0;
+        if (na) {
+            na->xfull[x] = int32_t(cnt[x] - tail);
+            na->xtail[x] = int32_t(tail);
+            na->xsplit[x] = int32_t(S);
+            na->xpbase[x] = int32_t(units);
+        }
+        units += tail * S;
+    }
+    return units;
+}
+
+// Big symmetric tiles per XCD of a group (each XCD takes a contiguous eighth of every
+// matrix's tiles). Returns the stage's K in 32-wide steps when every matrix of the
+// group has the same K (Gram: n_p, polynomial: m_p), else 0: with mixed K the last
+// tiles of an XCD are its shortest ones and splitting them was measured to cost more
+// than it saves.
+int64_t sym_xcd_counts(const GroupPlan& gp, bool gram, int64_t cnt[8]) {
+    for (int x = 0; x < 8; ++x) cnt[x] = 0;
+    int64_t k = -1;
+    for (const MatPlan& p : gp.mats) {
+        const int64_t t = p.m_p / kGemmBigM, T = t * (t + 1) / 2;
+        for (int x = 0; x < 8; ++x) cnt[x] += ((x + 1) * T >> 3) - (x * T >> 3);
+        const int64_t kp = gram ? p.n_p : p.m_p;
+        if (k < 0) k = kp;
+        else if (k != kp) k = 0;
+    }
+    return k > 0 ? k / 32 : 0;
+}
+
+int64_t sym_big_tiles(const GroupPlan& gp) {
+    int64_t big = 0;
+    for (const MatPlan& p : gp.mats) {
+        const int64_t t = p.m_p / kGemmBigM;
+        big += t * (t + 1) / 2;
+    }
+    return big;
+}
 
 struct Plan {
     std::vector<GroupPlan> groups;
@@ -139,6 +196,16 @@ int make_plan(const int64_t* rows, const int64_t* cols, int32_t count, Plan* pla
         if (cast_total >= tile_total_cap || rows_total >= tile_total_cap || col_total >= tile_total_cap ||
             upd_total >= tile_total_cap)
             return fail(MUON_ERR_TOO_LARGE, "a launch would exceed 2^31 workgroups");
+        if (kGemmTailSplit && kGemmBigM == kGemmBigN && sym_big_tiles(gp) >= kGemmBigMinTiles) {
+            int64_t cnt[8];
+            const int64_t kg = sym_xcd_counts(gp, true, cnt), kp = sym_xcd_counts(gp, false, cnt);
+            // both stages have the same tiles; either may split
+            gp.tail_units = std::max(kg ? tail_split(cnt, kg, nullptr) : 0, kp ? tail_split(cnt, kp, nullptr) : 0);
+            if (gp.tail_units > 0) {
+                gp.tail = ns;
+                ns = align256(ns + size_t(gp.tail_units) * kTailUnitFloats * 4);
+            }
+        }
         gp.bytes = std::max(ns, rn);
         plan->bytes = std::max(plan->bytes, gp.bytes);
         plan->groups.push_back(std::move(gp));
@@ -288,7 +355,9 @@ struct IoPtrs {
 // Fills tiles / tile_begin / total of a GEMM stage launch and returns the tile
 // configuration: the big tile when the stage has at least kGemmBigMinTiles of them
 // (symmetric stages need a square tile), the small one otherwise.
-GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym) {
+// ws != nullptr: a symmetric stage (Gram if gram, else the polynomial) may split its
+// tail tiles into the workspace's partial-tile region.
+GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym, char* ws = nullptr, bool gram = true) {
     const int ng = int(gp.mats.size());
     int64_t big = 0;
     for (int k = 0; k < ng; ++k) {
@@ -327,6 +396,22 @@ GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym) {
     }
     const int64_t tot = 8 * per_xcd_max;
     na.total = int32_t(tot);
+    na.tail = nullptr;
+    na.fix_total = 0;
+    if (sym && tile == kTileBig && ws != nullptr && gp.tail_units > 0) {
+        int64_t cnt[8], fix = 0, longest = 0;
+        const int64_t ks = sym_xcd_counts(gp, gram, cnt);
+        const int64_t units = ks ? tail_split(cnt, ks, &na) : 0;
+        if (units > 0 && units <= gp.tail_units) {
+            for (int x = 0; x < 8; ++x) {
+                fix += na.xtail[x];
+                longest = std::max<int64_t>(longest, int64_t(na.xfull[x]) + int64_t(na.xtail[x]) * na.xsplit[x]);
+            }
+            na.tail = reinterpret_cast<float*>(ws + gp.tail);
+            na.fix_total = int32_t(fix);
+            na.total = int32_t(8 * longest);
+        }
+    }
     return tile;
 }
 
@@ -411,9 +496,10 @@ int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_h
             d.tall = p.tall ? 1 : 0;
             d.upd_coef = float(double(hp.lr) * dir_scale(hp, p.n));
         }
-        const GemmTile sym_tile = plan_tiles(gp, na, true);
+        const GemmTile sym_tile = plan_tiles(gp, na, true, ws, true);
         rc = run_kernel(MUON_KCLASS_GRAM, s, "gram", [&] { return launch_ns_gemm(kModeGram, sym_tile, na, s); });
         if (rc) return rc;
+        plan_tiles(gp, na, true, ws, false);
         rc = run_kernel(MUON_KCLASS_POLY, s, "poly", [&] { return launch_ns_gemm(kModePoly, sym_tile, na, s); });
         if (rc) return rc;
         const GemmTile apply_tile = plan_tiles(gp, na, false);

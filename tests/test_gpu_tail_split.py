@@ -1,0 +1,85 @@
+"""GPU parity of the split tail of the symmetric NS5 stages.
+
+When a group's Gram or polynomial stage runs on 256-wide tiles and every matrix of
+the group has the same K for it, an XCD whose tile count leaves a last round of at
+most 16 tiles (of its 32 compute units) runs those tiles as K chunks that write fp32
+partial tiles; a fixup launch adds each tile's chunks in chunk order and applies the
+stage's epilogue. Two sets exercise it in both stages:
+  * 16 x [2048, 2048] (576 upper tiles): XCDs 1, 3, 5 and 7 hold 80 tiles and split
+    their last 16 (from matrices 12 to 15) in 2 chunks;
+  * 10 x [2560, 2560] (550 upper tiles): XCDs 1 to 7 hold 70 tiles and split their
+    last 6 (all from matrix 9) in 5 chunks; XCD 0 holds 60 and runs unsplit.
+The matrices with split tiles and the first one are checked against the float64
+oracle's Newton-Schulz at the bf16 tolerance, and each call is repeated to check
+that the fixed-order chunk sums make it bitwise repeatable. The split itself is
+recomputed here from the planning rule, so a change of rule that stops exercising
+it fails the test.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import muon_oracle as O
+from matrix_orthogonalising_optimizer_02_amd import binding as B
+from matrix_orthogonalising_optimizer_02_amd import workloads as WL
+from tolerances import NS_TOL
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ([(2048, 2048)] * 16, [0, 12, 13, 14, 15], {1: (16, 2), 3: (16, 2), 5: (16, 2), 7: (16, 2)}),
+    ([(2560, 2560)] * 10, [0, 9], {x: (6, 5) for x in range(1, 8)}),
+]
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def planned_split(shapes):
+    """XCD -> (tail tiles, chunks) by the library's rule for equal-K groups."""
+    cnt = [0] * 8
+    for a, b in shapes:
+        t = -(-min(a, b) // 256)
+        T = t * (t + 1) // 2
+        for x in range(8):
+            cnt[x] += ((x + 1) * T >> 3) - (x * T >> 3)
+    ksteps = -(-min(shapes[0]) // 256) * 256 // 32
+    out = {}
+    for x in range(8):
+        r = cnt[x] % 32
+        S = min(8, 32 // r, ksteps // 8) if 0 < r <= 16 else 1
+        if S >= 2:
+            out[x] = (r, S)
+    return out
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "the gpu tests need a visible GPU"
+    B.load_library()
+    return torch, torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_split_tail_tiles_vs_oracle_and_repeatable(torch_dev, case):
+    torch, dev = torch_dev
+    shapes, checked, split = CASES[case]
+    assert planned_split(shapes) == split
+    xs = [WL.host_normal(7 + case, WL.ROLE_G, i, s, 1e-3) for i, s in enumerate(shapes)]
+    ins = [torch.from_numpy(x.astype(np.float32)).to(dev) for x in xs]
+    log(f"ns5_batched: {len(shapes)} x {shapes[0]}, split tail tiles {split}")
+    outs = B.ns5_batched(ins)
+    outs2 = B.ns5_batched(ins)
+    torch.cuda.synchronize()
+    for i, (o, o2) in enumerate(zip(outs, outs2)):
+        assert torch.equal(o, o2), f"matrix {i}: two calls differ"
+    for i in checked:
+        ref = O.newton_schulz(xs[i].astype(np.float32).astype(np.float64))
+        oh = outs[i].detach().cpu().numpy().astype(np.float64)
+        err = float(np.linalg.norm(oh - ref) / np.linalg.norm(ref))
+        log(f"  matrix {i} {shapes[i]}: rel err {err:.3e}")
+        assert err < NS_TOL, (i, err)
