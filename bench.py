@@ -756,7 +756,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "k_ns_gemm<apply> (B X, iterations 1..4)",
                      "achieved": round(apply_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(apply_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("k_ns_gemm<2, muon::GemmCfg<256, 256, true, 32, 4> >", args.workload),
+                     "traffic": measured_traffic("k_ns_gemm<2, muon::GemmCfg<256, 256, true, 32, 4>, false>", args.workload),
                      "launch_ms": round(apply_launch_ms, 4), "launch_flops": apply_launch_flops},
         "kernels": kernels,
     }
