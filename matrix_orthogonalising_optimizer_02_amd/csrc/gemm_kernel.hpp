@@ -209,9 +209,10 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
     // K differ, and neighbouring tiles (shared operand panels) in the same L2. Blocks
     // left without a tile (the grid is 8 x the largest per-XCD count) exit here.
     constexpr bool kSym = (MODE == kModeGram || MODE == kModePoly);
-    // Tail split (symmetric stages on the direct-load tile): the XCD's blocks from
-    // xfull[x] on are chunk c of its tail tile xfull[x] + u / S, u = block - xfull[x].
-    constexpr bool kSplit = kSym && Cfg::kDirect && kSplitOK;
+    // Tail split (Gram, polynomial and non-final Apply on the direct-load tile): the
+    // XCD's blocks from xfull[x] on are chunk c of its tail tile xfull[x] + u / S,
+    // u = block - xfull[x].
+    constexpr bool kSplit = (kSym || MODE == kModeApply) && Cfg::kDirect && kSplitOK;
     int chunk = -1, nsplit = 1, unit = 0;
     int gi = -1, local = 0;
     {

@@ -6,9 +6,10 @@
 //          the small tile), K step 32 in a 4-deep ring of LDS stages filled by
 //          global_load_lds (three K steps of loads in flight), 128 KiB LDS, 1 block per CU.
 // The host picks, per stage, the big tile when the launch has enough big tiles to
-// fill the GPU, and the small one otherwise (small Gram matrices, small sets). A
-// symmetric stage on big tiles whose XCDs would end on a short last round runs those
-// last tiles as K chunks, and a fixup launch adds the chunks and applies the epilogue.
+// fill the GPU, and the small one otherwise (small Gram matrices, small sets). A Gram,
+// polynomial or non-final Apply stage on big tiles whose XCDs would end on a short last
+// round runs those last tiles as K chunks, and a fixup launch adds the chunks and
+// applies the epilogue.
 #include "gemm_kernel.hpp"
 
 #ifndef MUON_GEMM_BIG_DIRECT
@@ -34,12 +35,15 @@ __global__ __launch_bounds__(256, (Cfg::kLdsBytes > 80 * 1024) ? 1 : 2) void k_n
     ns_gemm_tile<MODE, Cfg, SPLIT>(args, smem);
 }
 
-// Fixup of the split tail tiles of a symmetric stage (big tiles: 2 x 2 waves of 4 x 4
-// blocks of 32 x 32). Each thread takes 4 consecutive accumulator lanes of one wave and
-// register index of one tail tile, adds the tile's chunks in chunk order and applies the
-// stage's epilogue arithmetic: Gram A = s2 * acc, polynomial B = b A + c * acc (A read
-// at the mirrored position, as in the tile epilogue), bf16, stored at (i, j) and, off
-// the diagonal, at (j, i). kTailUnitFloats / 1024 blocks per tail tile.
+// Fixup of the split tail tiles of a stage (big tiles: 2 x 2 waves of 4 x 4 blocks of
+// 32 x 32). Each thread takes 4 consecutive accumulator lanes of one wave and register
+// index of one tail tile, adds the tile's chunks in chunk order and applies the stage's
+// epilogue arithmetic, as the tile epilogue does:
+//   Gram        A = s2 acc, bf16 at (i, j) and, off the diagonal, at (j, i);
+//   polynomial  B = b A + c acc (A read at (j, i)), stored the same way;
+//   Apply       X' = s1 (a X + acc) (X read from X_c at (j, i)), bf16 into X'_c at
+//               (j, i) and into the row-major X'_r at (i, j) when the next Gram reads it.
+// kTailUnitFloats / 1024 blocks per tail tile.
 template <int MODE>
 __global__ __launch_bounds__(256) void k_ns_tail_fix(NsArgs args) {
     using Cfg = BigCfg;
@@ -56,7 +60,8 @@ __global__ __launch_bounds__(256) void k_ns_tail_fix(NsArgs args) {
     if (gi < 0) return;
     const NsDesc& d = args.d[gi];
     int ti, tj;
-    tri_tile(local, d.tiles, ti, tj);
+    if constexpr (MODE == kModeApply) rect_tile(local, d.m_p / 256, d.tiles, ti, tj);
+    else tri_tile(local, d.tiles, ti, tj);
     const float* src = args.tail + (int64_t)(args.xpbase[x] + t * S) * kTailUnitFloats + e;
     floatx4 v = *reinterpret_cast<const floatx4*>(src);
     for (int c = 1; c < S; ++c) {
@@ -69,17 +74,25 @@ __global__ __launch_bounds__(256) void k_ns_tail_fix(NsArgs args) {
     const int a = idx >> 6, b = (idx >> 4) & 3, r = idx & 15;
     const int i = ti * 256 + (wave >> 1) * 128 + a * 32 + 8 * (r >> 2) + 4 * (lane0 >> 5) + (r & 3);
     const int64_t ld = d.m_p;
-    unsigned short* dst = (MODE == kModeGram) ? d.a : d.b;
-    const float g2 = (MODE == kModeGram && args.first) ? (*d.scale) * (*d.scale) : 1.0f;
+    const float s1 = args.first ? *d.scale : 1.0f;
+    const float g2 = s1 * s1;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int j = tj * 256 + (wave & 1) * 128 + b * 32 + ((lane0 + q) & 31);
         float y = v[q];
-        if constexpr (MODE == kModeGram) y *= g2;
-        else y = fmaf(args.cb, bf2f(d.a[kb_off(j, i, ld)]), args.cc * y);
-        const unsigned short h = f2bf(y);
-        dst[kb_off(i, j, ld)] = h;
-        if (ti != tj) dst[kb_off(j, i, ld)] = h;
+        if constexpr (MODE == kModeApply) {
+            y = fmaf(args.ca, bf2f(d.xc[kb_off(j, i, ld)]), y) * s1;
+            const unsigned short h = f2bf(y);
+            d.xc_next[kb_off(j, i, ld)] = h;
+            if (d.xr_next) d.xr_next[(int64_t)i * d.n_p + j] = h;
+        } else {
+            unsigned short* dst = (MODE == kModeGram) ? d.a : d.b;
+            if constexpr (MODE == kModeGram) y *= g2;
+            else y = fmaf(args.cb, bf2f(d.a[kb_off(j, i, ld)]), args.cc * y);
+            const unsigned short h = f2bf(y);
+            dst[kb_off(i, j, ld)] = h;
+            if (ti != tj) dst[kb_off(j, i, ld)] = h;
+        }
     }
 }
 
@@ -99,7 +112,7 @@ static hipError_t launch_cfg(GemmMode mode, const NsArgs& a, hipStream_t s) {
 hipError_t launch_ns_gemm(GemmMode mode, GemmTile tile, const NsArgs& a, hipStream_t s) {
     if (tile != kTileBig) return launch_cfg<SmallCfg>(mode, a, s);
     if (a.tail == nullptr || a.fix_total <= 0) return launch_cfg<BigCfg>(mode, a, s);
-    // a symmetric stage that splits its tail tiles: the tiles and chunks, then the fixup
+    // a stage that splits its tail tiles: the tiles and chunks, then the fixup
     // that adds the chunks and applies the epilogue
     const dim3 grid(a.total), block(BigCfg::NT), fgrid(a.fix_total * (kTailUnitFloats / 1024));
     if (mode == kModeGram) {
@@ -108,6 +121,9 @@ hipError_t launch_ns_gemm(GemmMode mode, GemmTile tile, const NsArgs& a, hipStre
     } else if (mode == kModePoly) {
         hipLaunchKernelGGL((k_ns_gemm<kModePoly, BigCfg, true>), grid, block, 0, s, a);
         hipLaunchKernelGGL(k_ns_tail_fix<kModePoly>, fgrid, dim3(256), 0, s, a);
+    } else if (mode == kModeApply) {
+        hipLaunchKernelGGL((k_ns_gemm<kModeApply, BigCfg, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL(k_ns_tail_fix<kModeApply>, fgrid, dim3(256), 0, s, a);
     } else {
         return hipErrorInvalidValue;
     }

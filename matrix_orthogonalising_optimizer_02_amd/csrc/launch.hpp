@@ -74,7 +74,8 @@ struct NsDesc {
     float* part;           // final modes, optional: [ntiles * 4] per-wave sums of O^2
 };
 
-// Symmetric stages on big tiles may split the last round of tiles of an XCD: its
+// Gram, polynomial and non-final Apply stages on big tiles may split the last round of
+// tiles of an XCD: its
 // sequence of tiles ends with xtail[x] tiles that run as xsplit[x] chunks of K each
 // (blocks xfull[x] .. xfull[x] + xtail[x] * xsplit[x] - 1 of the XCD), writing fp32
 // partial tiles (kTailUnitFloats each, accumulator order) at tail + (xpbase[x] + u) *

@@ -75,54 +75,75 @@ struct GroupPlan {
 // MI355X: 256 compute units in 8 XCDs; a big-tile block fills one compute unit.
 constexpr int kCusPerXcd = 32;
 
-// Tail split of a symmetric stage on big tiles. XCD x runs cnt[x] tiles in rounds of
+// Tail split of a GEMM stage on big tiles. XCD x runs cnt[x] tiles in rounds of
 // kCusPerXcd blocks; a last round of r <= kCusPerXcd / 2 tiles would leave most of the
 // XCD idle while it runs, so those r tiles run as S chunks of K each (S r <= kCusPerXcd,
-// S <= kTailMaxSplit, chunks cut at multiples of 256 of K, i.e. of 8 K steps). Returns
-// the number of partial tiles (0: no split).
-int64_t tail_split(const int64_t cnt[8], int64_t min_ksteps, NsArgs* na) {
-    int64_t units = 0;
+// S <= kTailMaxSplit, chunks cut at multiples of 256 of K, i.e. of 8 K steps). The split
+// is taken only when the time it saves, (1 - 1 / S) of a tile for the XCD that splits
+// least, exceeds what its partial tiles cost (one fp32 tile written and read per chunk,
+// plus the fixup launch); the constants are measured on MI355X. Returns the number of
+// partial tiles (0: no split).
+constexpr double kTailStepUs = 0.86;   // one 32-wide K step of a 256 x 256 tile
+constexpr double kTailUnitUs = 0.13;   // 512 KiB of partial-tile traffic
+constexpr double kTailFixedUs = 10.0;  // the fixup launch
+int64_t tail_split(const int64_t cnt[8], int64_t ksteps, NsArgs* na) {
+    int64_t S[8], tail[8], units = 0, s_min = kTailMaxSplit;
     for (int x = 0; x < 8; ++x) {
         const int64_t r = cnt[x] % kCusPerXcd;
-        int64_t S = 1;
+        S[x] = 1;
         if (r > 0 && r <= kCusPerXcd / 2)
-            S = std::min<int64_t>({kTailMaxSplit, kCusPerXcd / r, min_ksteps / 8});
-        if (S < 2) S = 1;
-        const int64_t tail = S > 1 ? r : 0;
-        if (na) {
-            na->xfull[x] = int32_t(cnt[x] - tail);
-            na->xtail[x] = int32_t(tail);
-            na->xsplit[x] = int32_t(S);
-            na->xpbase[x] = int32_t(units);
+            S[x] = std::min<int64_t>({kTailMaxSplit, kCusPerXcd / r, ksteps / 8});
+        if (S[x] < 2) S[x] = 1;
+        tail[x] = S[x] > 1 ? r : 0;
+        if (tail[x]) s_min = std::min(s_min, S[x]);
+        units += tail[x] * S[x];
+    }
+    const double saved = (1.0 - 1.0 / double(s_min)) * double(ksteps) * kTailStepUs;
+    if (units == 0 || saved <= double(units) * kTailUnitUs + kTailFixedUs) {
+        units = 0;
+        for (int x = 0; x < 8; ++x) { S[x] = 1; tail[x] = 0; }
+    }
+    if (na) {
+        int64_t base = 0;
+        for (int x = 0; x < 8; ++x) {
+            na->xfull[x] = int32_t(cnt[x] - tail[x]);
+            na->xtail[x] = int32_t(tail[x]);
+            na->xsplit[x] = int32_t(S[x]);
+            na->xpbase[x] = int32_t(base);
+            base += tail[x] * S[x];
         }
-        units += tail * S;
     }
     return units;
 }
 
-// Big symmetric tiles per XCD of a group (each XCD takes a contiguous eighth of every
-// matrix's tiles). Returns the stage's K in 32-wide steps when every matrix of the
-// group has the same K (Gram: n_p, polynomial: m_p), else 0: with mixed K the last
-// tiles of an XCD are its shortest ones and splitting them was measured to cost more
-// than it saves.
-int64_t sym_xcd_counts(const GroupPlan& gp, bool gram, int64_t cnt[8]) {
+enum SplitStage : int { kStageGram = 0, kStagePoly = 1, kStageApply = 2 };
+
+// Big tiles per XCD of a stage of a group (each XCD takes a contiguous eighth of every
+// matrix's tiles: upper-triangle tiles for the Gram and polynomial, all tiles of X' for
+// the Apply). Returns the stage's K in 32-wide steps when every matrix of the group has
+// the same K (Gram: n_p; polynomial and Apply: m_p), else 0: with mixed K the last tiles
+// of an XCD are its shortest ones and splitting them was measured to cost more than it
+// saves.
+int64_t xcd_counts(const GroupPlan& gp, int stage, int64_t cnt[8]) {
     for (int x = 0; x < 8; ++x) cnt[x] = 0;
     int64_t k = -1;
     for (const MatPlan& p : gp.mats) {
-        const int64_t t = p.m_p / kGemmBigM, T = t * (t + 1) / 2;
+        const int64_t t = p.m_p / kGemmBigM;
+        const int64_t T = stage == kStageApply ? t * (p.n_p / kGemmBigN) : t * (t + 1) / 2;
         for (int x = 0; x < 8; ++x) cnt[x] += ((x + 1) * T >> 3) - (x * T >> 3);
-        const int64_t kp = gram ? p.n_p : p.m_p;
+        const int64_t kp = stage == kStageGram ? p.n_p : p.m_p;
         if (k < 0) k = kp;
         else if (k != kp) k = 0;
     }
     return k > 0 ? k / 32 : 0;
 }
 
-int64_t sym_big_tiles(const GroupPlan& gp) {
+// Big tiles of a stage: the rule that picks the big tile for it (see plan_tiles).
+int64_t big_tiles(const GroupPlan& gp, bool sym) {
     int64_t big = 0;
     for (const MatPlan& p : gp.mats) {
         const int64_t t = p.m_p / kGemmBigM;
-        big += t * (t + 1) / 2;
+        big += sym ? t * (t + 1) / 2 : t * (p.n_p / kGemmBigN);
     }
     return big;
 }
@@ -196,11 +217,16 @@ int make_plan(const int64_t* rows, const int64_t* cols, int32_t count, Plan* pla
         if (cast_total >= tile_total_cap || rows_total >= tile_total_cap || col_total >= tile_total_cap ||
             upd_total >= tile_total_cap)
             return fail(MUON_ERR_TOO_LARGE, "a launch would exceed 2^31 workgroups");
-        if (kGemmTailSplit && kGemmBigM == kGemmBigN && sym_big_tiles(gp) >= kGemmBigMinTiles) {
+        if (kGemmTailSplit) {
+            // the partial-tile region serves whichever stage splits the most tiles
             int64_t cnt[8];
-            const int64_t kg = sym_xcd_counts(gp, true, cnt), kp = sym_xcd_counts(gp, false, cnt);
-            // both stages have the same tiles; either may split
-            gp.tail_units = std::max(kg ? tail_split(cnt, kg, nullptr) : 0, kp ? tail_split(cnt, kp, nullptr) : 0);
+            gp.tail_units = 0;
+            for (int st = kStageGram; st <= kStageApply; ++st) {
+                const bool sym = st != kStageApply;
+                if ((sym && kGemmBigM != kGemmBigN) || big_tiles(gp, sym) < kGemmBigMinTiles) continue;
+                const int64_t ks = xcd_counts(gp, st, cnt);
+                if (ks) gp.tail_units = std::max(gp.tail_units, tail_split(cnt, ks, nullptr));
+            }
             if (gp.tail_units > 0) {
                 gp.tail = ns;
                 ns = align256(ns + size_t(gp.tail_units) * kTailUnitFloats * 4);
@@ -355,9 +381,9 @@ struct IoPtrs {
 // Fills tiles / tile_begin / total of a GEMM stage launch and returns the tile
 // configuration: the big tile when the stage has at least kGemmBigMinTiles of them
 // (symmetric stages need a square tile), the small one otherwise.
-// ws != nullptr: a symmetric stage (Gram if gram, else the polynomial) may split its
-// tail tiles into the workspace's partial-tile region.
-GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym, char* ws = nullptr, bool gram = true) {
+// ws != nullptr: the stage (Gram, polynomial or a non-final Apply) may split its tail
+// tiles into the workspace's partial-tile region.
+GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym, char* ws = nullptr, int stage = kStageGram) {
     const int ng = int(gp.mats.size());
     int64_t big = 0;
     for (int k = 0; k < ng; ++k) {
@@ -398,9 +424,9 @@ GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym, char* ws = nullpt
     na.total = int32_t(tot);
     na.tail = nullptr;
     na.fix_total = 0;
-    if (sym && tile == kTileBig && ws != nullptr && gp.tail_units > 0) {
+    if (tile == kTileBig && ws != nullptr && gp.tail_units > 0) {
         int64_t cnt[8], fix = 0, longest = 0;
-        const int64_t ks = sym_xcd_counts(gp, gram, cnt);
+        const int64_t ks = xcd_counts(gp, stage, cnt);
         const int64_t units = ks ? tail_split(cnt, ks, &na) : 0;
         if (units > 0 && units <= gp.tail_units) {
             for (int x = 0; x < 8; ++x) {
@@ -496,13 +522,14 @@ int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_h
             d.tall = p.tall ? 1 : 0;
             d.upd_coef = float(double(hp.lr) * dir_scale(hp, p.n));
         }
-        const GemmTile sym_tile = plan_tiles(gp, na, true, ws, true);
+        const GemmTile sym_tile = plan_tiles(gp, na, true, ws, kStageGram);
         rc = run_kernel(MUON_KCLASS_GRAM, s, "gram", [&] { return launch_ns_gemm(kModeGram, sym_tile, na, s); });
         if (rc) return rc;
-        plan_tiles(gp, na, true, ws, false);
+        plan_tiles(gp, na, true, ws, kStagePoly);
         rc = run_kernel(MUON_KCLASS_POLY, s, "poly", [&] { return launch_ns_gemm(kModePoly, sym_tile, na, s); });
         if (rc) return rc;
-        const GemmTile apply_tile = plan_tiles(gp, na, false);
+        // the last Apply (fused update or fp32 O) keeps every tile whole
+        const GemmTile apply_tile = plan_tiles(gp, na, false, last ? nullptr : ws, kStageApply);
         const GemmMode mode = !last ? kModeApply : ((update_w && !eq6) ? kModeFinalW : kModeFinalO);
         rc = run_kernel(last ? MUON_KCLASS_APPLY_FINAL : MUON_KCLASS_APPLY, s, "apply",
                         [&] { return launch_ns_gemm(mode, apply_tile, na, s); });

@@ -1,14 +1,21 @@
-"""GPU parity of the split tail of the symmetric NS5 stages.
+"""GPU parity of the split tail of the NS5 GEMM stages.
 
-When a group's Gram or polynomial stage runs on 256-wide tiles and every matrix of
-the group has the same K for it, an XCD whose tile count leaves a last round of at
-most 16 tiles (of its 32 compute units) runs those tiles as K chunks that write fp32
-partial tiles; a fixup launch adds each tile's chunks in chunk order and applies the
-stage's epilogue. Two sets exercise it in both stages:
-  * 16 x [2048, 2048] (576 upper tiles): XCDs 1, 3, 5 and 7 hold 80 tiles and split
-    their last 16 (from matrices 12 to 15) in 2 chunks;
-  * 10 x [2560, 2560] (550 upper tiles): XCDs 1 to 7 hold 70 tiles and split their
-    last 6 (all from matrix 9) in 5 chunks; XCD 0 holds 60 and runs unsplit.
+When a group's Gram, polynomial or non-final Apply stage runs on 256-wide tiles and
+every matrix of the group has the same K for it, an XCD whose tile count leaves a last
+round of at most 16 tiles (of its 32 compute units) runs those tiles as K chunks that
+write fp32 partial tiles; a fixup launch adds each tile's chunks in chunk order and
+applies the stage's epilogue. The split is taken only when the modelled time it saves
+exceeds the cost of its partial tiles (the library's planning rule, mirrored below).
+Three sets exercise it:
+  * 16 x [2048, 2048] (576 upper tiles): in the Gram and polynomial, XCDs 1, 3, 5 and
+    7 hold 80 tiles and split their last 16 (from matrices 12 to 15) in 2 chunks; the
+    Apply (128 tiles per XCD) does not split;
+  * 10 x [2560, 2560] (550 upper tiles): in the Gram and polynomial, XCDs 1 to 7 hold
+    70 tiles and split their last 6 (all from matrix 9) in 5 chunks; in the Apply,
+    XCDs 1, 3, 5 and 7 hold 130 tiles and split their last 2 (matrix 9) in 8 chunks;
+  * [2048, 8448] and [8448, 2048]: the Gram and polynomial run on 128-wide tiles (72
+    big upper tiles), so the Apply also writes the row-major X'_r; every XCD holds 66
+    Apply tiles and splits its last 2 (from the second matrix) in 8 chunks.
 The matrices with split tiles and the first one are checked against the float64
 oracle's Newton-Schulz at the bf16 tolerance, and each call is repeated to check
 that the fixed-order chunk sums make it bitwise repeatable. The split itself is
@@ -27,9 +34,12 @@ from tolerances import NS_TOL
 
 pytestmark = pytest.mark.gpu
 
+# shapes, matrices checked against the oracle, split of the symmetric stages (XCD ->
+# (tail tiles, chunks)), split of the Apply
 CASES = [
-    ([(2048, 2048)] * 16, [0, 12, 13, 14, 15], {1: (16, 2), 3: (16, 2), 5: (16, 2), 7: (16, 2)}),
-    ([(2560, 2560)] * 10, [0, 9], {x: (6, 5) for x in range(1, 8)}),
+    ([(2048, 2048)] * 16, [0, 12, 13, 14, 15], {1: (16, 2), 3: (16, 2), 5: (16, 2), 7: (16, 2)}, {}),
+    ([(2560, 2560)] * 10, [0, 9], {x: (6, 5) for x in range(1, 8)}, {1: (2, 8), 3: (2, 8), 5: (2, 8), 7: (2, 8)}),
+    ([(2048, 8448), (8448, 2048)], [0, 1], {}, {x: (2, 8) for x in range(8)}),
 ]
 
 
@@ -38,14 +48,20 @@ def log(msg):
     sys.stdout.flush()
 
 
-def planned_split(shapes):
-    """XCD -> (tail tiles, chunks) by the library's rule for equal-K groups."""
+def planned_split(shapes, apply=False):
+    """XCD -> (tail tiles, chunks) by the library's rule, for a group whose matrices
+    share the stage's K (m for the polynomial and Apply; these sets also share n where
+    the Gram splits). No split when the stage runs on 128-wide tiles."""
     cnt = [0] * 8
+    big = 0
     for a, b in shapes:
         t = -(-min(a, b) // 256)
-        T = t * (t + 1) // 2
+        T = t * (-(-max(a, b) // 256)) if apply else t * (t + 1) // 2
+        big += T
         for x in range(8):
             cnt[x] += ((x + 1) * T >> 3) - (x * T >> 3)
+    if big < 512:
+        return {}
     ksteps = -(-min(shapes[0]) // 256) * 256 // 32
     out = {}
     for x in range(8):
@@ -53,7 +69,12 @@ def planned_split(shapes):
         S = min(8, 32 // r, ksteps // 8) if 0 < r <= 16 else 1
         if S >= 2:
             out[x] = (r, S)
-    return out
+    if not out:
+        return out
+    units = sum(r * S for r, S in out.values())
+    s_min = min(S for _, S in out.values())
+    saved = (1.0 - 1.0 / s_min) * ksteps * 0.86
+    return out if saved > units * 0.13 + 10.0 else {}
 
 
 @pytest.fixture(scope="module")
@@ -67,11 +88,12 @@ def torch_dev():
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_split_tail_tiles_vs_oracle_and_repeatable(torch_dev, case):
     torch, dev = torch_dev
-    shapes, checked, split = CASES[case]
+    shapes, checked, split, split_apply = CASES[case]
     assert planned_split(shapes) == split
+    assert planned_split(shapes, apply=True) == split_apply
     xs = [WL.host_normal(7 + case, WL.ROLE_G, i, s, 1e-3) for i, s in enumerate(shapes)]
     ins = [torch.from_numpy(x.astype(np.float32)).to(dev) for x in xs]
-    log(f"ns5_batched: {len(shapes)} x {shapes[0]}, split tail tiles {split}")
+    log(f"ns5_batched: {shapes}, split tail tiles {split}, Apply {split_apply}")
     outs = B.ns5_batched(ins)
     outs2 = B.ns5_batched(ins)
     torch.cuda.synchronize()
