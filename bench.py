@@ -58,7 +58,9 @@ def apply_flops(m, n):
 
 
 def measured_traffic(kernel, workload_key):
-    """HBM bytes per dispatch of `kernel` from the committed rocprofv3 counter summary.
+    """HBM bytes per dispatch of `kernel` from the committed rocprofv3 counter summary
+    (a list of names: the first kernel plus the others that run with it, e.g. a split
+    stage's fixup).
 
     The summary records FETCH_SIZE / WRITE_SIZE per dispatch, the copy-kernel
     calibration factors and a hash of the GEMM sources; a changed kernel (or another
@@ -77,8 +79,11 @@ def measured_traffic(kernel, workload_key):
             h.update(fh.read())
     if h.hexdigest() != rec["gemm_source_sha256"]:
         return None
-    entry = rec["kernels"].get(kernel)
-    return None if entry is None else entry["hbm_bytes_per_dispatch"]
+    kernels = [kernel] if isinstance(kernel, str) else list(kernel)
+    entries = [rec["kernels"].get(k) for k in kernels]
+    if entries[0] is None:
+        return None
+    return sum(e["hbm_bytes_per_dispatch"] for e in entries if e is not None)
 
 
 GEMM_SOURCES = ["gemm_kernel.hpp", "k_gemm.hip", "launch.hpp", "common.hpp"]
@@ -753,10 +758,11 @@ def main():
             "periodic_over_vanilla": round((cycle_ms / k) / vanilla_ms, 4),
             "pages_periodic_over_vanilla_15b": round(1.317 / 2.884, 4),
             "note": "one MI355X, optimizer step only, no communication"}),
-        "roofline": {"bound": "mfma", "kernel": "k_ns_gemm<apply> (B X, iterations 1..4)",
+        "roofline": {"bound": "mfma", "kernel": "k_ns_gemm<apply> (B X, iterations 1..4; with its tail fixup where split)",
                      "achieved": round(apply_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(apply_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("k_ns_gemm<2, muon::GemmCfg<256, 256, true, 32, 4>, false>", args.workload),
+                     "traffic": measured_traffic(["k_ns_gemm<2, muon::GemmCfg<256, 256, true, 32, 4>, true>",
+                                                  "k_ns_tail_fix<2>"], args.workload),
                      "launch_ms": round(apply_launch_ms, 4), "launch_flops": apply_launch_flops},
         "kernels": kernels,
     }
