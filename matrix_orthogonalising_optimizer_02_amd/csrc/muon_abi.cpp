@@ -68,7 +68,7 @@ struct MatPlan {
 struct GroupPlan {
     std::vector<MatPlan> mats;
     size_t bytes = 0;
-    size_t tail = 0;          // fp32 partial tiles of the split symmetric stages
+    size_t tail = 0;          // fp32 partial tiles of the stages that split their tail
     int64_t tail_units = 0;
 };
 
