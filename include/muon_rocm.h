@@ -94,9 +94,9 @@ typedef struct muon_matrix {
 /* Kernel classes reported by the optional timing facility. */
 #define MUON_KCLASS_CAST 0          /* momentum + Frobenius partials + bf16 working copies */
 #define MUON_KCLASS_FROB 1          /* per-matrix 1 / max(||M||_F, eps) */
-#define MUON_KCLASS_GRAM 2          /* A = X X^T (symmetric tiles, bf16 MFMA) */
-#define MUON_KCLASS_POLY 3          /* B = b A + c A A (symmetric tiles, bf16 MFMA) */
-#define MUON_KCLASS_APPLY 4         /* X' = a X + B X, iterations 1..N-1 */
+#define MUON_KCLASS_GRAM 2          /* A = X X^T (symmetric tiles, bf16 MFMA; with its tail fixup) */
+#define MUON_KCLASS_POLY 3          /* B = b A + c A A (symmetric tiles, bf16 MFMA; with its tail fixup) */
+#define MUON_KCLASS_APPLY 4         /* X' = a X + B X, iterations 1..N-1 (with its tail fixup) */
 #define MUON_KCLASS_APPLY_FINAL 5   /* last iteration: O out, or the fused Eq. 4 update */
 #define MUON_KCLASS_ROWNORM_ROWS 6  /* one-pass RowNorm step, flat / square matrices */
 #define MUON_KCLASS_COLNORM_PARTIAL 7  /* tall: momentum + per-column partial sums */
@@ -289,7 +289,9 @@ int svd_entropy(const float* const* w, const int64_t* rows, const int64_t* cols,
                 void* stream);
 
 /* Optional per-kernel-class timing. While enabled (enable != 0), every kernel the
- * library enqueues is bracketed by HIP events recorded on the caller's stream.
+ * library enqueues is bracketed by HIP events recorded on the caller's stream (a GEMM
+ * stage that splits its last tiles over K is bracketed together with its fixup
+ * launch, and counts as one launch).
  * muon_timing_read() waits for the recorded events, adds their durations into
  * ms[MUON_KCLASS_COUNT] and launch counts into launches[MUON_KCLASS_COUNT] (either
  * may be NULL), and clears the record. muon_timing_enable(0) discards the record.
