@@ -12,8 +12,10 @@ Prints ONE JSON line. `value` is the mean time of one Muon optimizer step
 averaged over the Periodic cycle (ms, lower is better); `ms_per_step` is the time
 of one whole cycle. Also reported: the vanilla (every step NS5) step time, NS5
 TFLOP/s, RowNorm GB/s, the dominant kernel against its roofline (per-launch
-HIP-event durations recorded by the library on the launch stream), and the
-float64 oracle timed on a bounded sample on the host cores.
+HIP-event durations recorded by the library on the launch stream), the same step
+figures for the other multi-matrix workloads (the H = 2048 DiT block, the 16-matrix
+bucket, the H = 3072 MMDiT pair), and the float64 oracle timed on a bounded sample on
+the host cores.
 """
 from __future__ import annotations
 
