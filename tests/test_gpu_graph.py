@@ -42,8 +42,12 @@ def make_state(torch, dev, shapes, key):
     return w, m, g
 
 
+# the last set runs its Gram, polynomial and Apply stages with split tail tiles and
+# their fixup launches (ten [2560, 2560] matrices: XCDs with 70 upper tiles split 6 in
+# 5 chunks, XCDs with 130 Apply tiles split 2 in 8)
 @pytest.mark.parametrize("shapes", [[(128, 512)],
-                                    [(768, 256), (256, 256), (1024, 256), (256, 1024), (1536, 256)]])
+                                    [(768, 256), (256, 256), (1024, 256), (256, 1024), (1536, 256)],
+                                    [(2560, 2560)] * 10])
 def test_captured_periodic_cycle_replays_bitwise(torch_dev, shapes):
     torch, dev = torch_dev
     hp = B.default_hparams(period_k=3)
