@@ -9,15 +9,15 @@ Sources (the pages this follows; sections named, no line numbers):
         Sec. 2.1 Eq. 1 (momentum, Newton-Schulz, plain update), the Newton-Schulz
         paragraph with Eq. 2 and the coefficients a, b, c; Sec. 2.2 Eq. 3 (weight
         decay), Lemma 1 (update RMS), Eq. 4 (0.2 * sqrt(max(A,B)) scale), and the
-        "other hyper-parameters" paragraph (N = 5, mu = 0.95).
+        paragraph on the remaining hyper-parameters (N = 5, mu = 0.95).
   [DiT] "Scaling Muon for Diffusion Transformers" (summary page): the Periodic
         Row-wise Muon paragraphs (NS5 once every K steps, RowNorm of the current
         momentum on the other steps, K = 3, gamma = 0.15, gamma = 1 means reusing
         the Muon learning rate) and the distributed-implementation paragraph
         (rows of flat matrices are shard-local; tall matrices reduce per-column norms).
-  [ABS] The same paper's abstract page: "a full NS5 spectral update once every K
-        steps and a row-wise constrained update based on the current momentum at
-        the remaining steps".
+  [ABS] The same paper's abstract page: the full NS5 update runs once in every K
+        steps, and the steps in between take a row-wise constrained update of the
+        momentum as it stands at that step.
 
 Readings taken where the pages are silent (each is also listed in the design notes):
   R1  The Periodic non-refresh update is Eq. 4 with O replaced by gamma * RowNorm(M_t).
