@@ -396,7 +396,24 @@ GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym, char* ws = nullpt
         }
     }
     const bool big_ok = !sym || kGemmBigM == kGemmBigN;
-    const GemmTile tile = (big_ok && big >= kGemmBigMinTiles) ? kTileBig : kTileSmall;
+    GemmTile tile = (big_ok && big >= kGemmBigMinTiles) ? kTileBig : kTileSmall;
+    // The polynomial's K is m, short next to the Gram's n: when its big tiles fit in one
+    // round on every XCD while the small ones would need more than one (two small blocks
+    // share a compute unit), the big tile is faster (measured at the H = 2048 block: 180
+    // big tiles, 0.080 -> 0.068 ms per launch).
+    if (sym && stage == kStagePoly && tile == kTileSmall && big_ok) {
+        int64_t cb[8] = {0}, cs[8] = {0};
+        for (int k = 0; k < ng; ++k) {
+            const int64_t tb = gp.mats[k].m_p / kGemmBigM, ts = gp.mats[k].m_p / kGemmSmall;
+            const int64_t Tb = tb * (tb + 1) / 2, Ts = ts * (ts + 1) / 2;
+            for (int x = 0; x < 8; ++x) {
+                cb[x] += ((x + 1) * Tb >> 3) - (x * Tb >> 3);
+                cs[x] += ((x + 1) * Ts >> 3) - (x * Ts >> 3);
+            }
+        }
+        const int64_t mb = *std::max_element(cb, cb + 8), ms = *std::max_element(cs, cs + 8);
+        if (mb > 0 && mb <= kCusPerXcd && ms > 2 * kCusPerXcd) tile = kTileBig;
+    }
     const int64_t bm = tile == kTileBig ? kGemmBigM : kGemmSmall;
     const int64_t bn = tile == kTileBig ? kGemmBigN : kGemmSmall;
     for (int k = 0; k < ng; ++k) {
@@ -525,8 +542,8 @@ int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_h
         const GemmTile sym_tile = plan_tiles(gp, na, true, ws, kStageGram);
         rc = run_kernel(MUON_KCLASS_GRAM, s, "gram", [&] { return launch_ns_gemm(kModeGram, sym_tile, na, s); });
         if (rc) return rc;
-        plan_tiles(gp, na, true, ws, kStagePoly);
-        rc = run_kernel(MUON_KCLASS_POLY, s, "poly", [&] { return launch_ns_gemm(kModePoly, sym_tile, na, s); });
+        const GemmTile poly_tile = plan_tiles(gp, na, true, ws, kStagePoly);
+        rc = run_kernel(MUON_KCLASS_POLY, s, "poly", [&] { return launch_ns_gemm(kModePoly, poly_tile, na, s); });
         if (rc) return rc;
         // the last Apply (fused update or fp32 O) keeps every tile whole
         const GemmTile apply_tile = plan_tiles(gp, na, false, last ? nullptr : ws, kStageApply);
