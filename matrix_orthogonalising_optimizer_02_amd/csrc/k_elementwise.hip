@@ -307,8 +307,9 @@ __global__ __launch_bounds__(256) void k_colnorm_partial(ColArgs args) {
     const float mu = args.mu;
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
     if (VEC && c0 + 3 < d.cols) {
-        // rows in batches of kB, loads ahead of stores
-        constexpr int kB = 8;
+        // rows in batches of kB, loads ahead of stores (16: each wave's 64 rows of the
+        // chunk in one batch; measured 0.6-1% faster than 8, 4 slower)
+        constexpr int kB = 16;
         for (int rb = r0 + wave; rb < r1; rb += 4 * kB) {
             floatx4 mv[kB], gv[kB];
 #pragma unroll
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(256) void k_colnorm_apply(ColArgs args) {
         floatx4 kc;
 #pragma unroll
         for (int e = 0; e < 4; ++e) kc[e] = d.coef * iv[e];
-        constexpr int kB = 8;
+        constexpr int kB = 16;
         for (int rb = r0 + wave; rb < r1; rb += 4 * kB) {
             floatx4 mv[kB], wv[kB];
 #pragma unroll
