@@ -92,6 +92,26 @@ def test_ns5_more_than_one_group_and_mixed_m(torch_dev):
     assert max(errs) < NS_TOL
 
 
+def test_ns5_apply_on_one_round_of_big_tiles(torch_dev):
+    """Three [2048, 2048] matrices: 192 big Apply tiles (24 per XCD, one round) against 768
+    small ones (96 per XCD, two rounds), so the Apply runs on 256-wide tiles, the Gram
+    and polynomial on 128-wide ones. Against the oracle at the bf16 tolerance; and equal
+    bit for bit to the same matrix alone (192 / 3 = 64 big tiles, 256 small ones: 8 and
+    32 per XCD, so it stays on 128-wide tiles), since both tiles accumulate over K in the
+    same order."""
+    torch, dev = torch_dev
+    shapes = [(2048, 2048)] * 3
+    xs = [gauss(104, i, s) for i, s in enumerate(shapes)]
+    outs = B.ns5_batched([to_dev(torch, dev, x) for x in xs])
+    alone = B.ns5_batched([to_dev(torch, dev, xs[2])])
+    torch.cuda.synchronize()
+    assert torch.equal(outs[2], alone[0])
+    for i in (0, 2):
+        err = rel_fro(to_host(outs[i]), O.newton_schulz(xs[i]))
+        log(f"  three [2048, 2048], matrix {i}: rel err {err:.3e}")
+        assert err < NS_TOL, (i, err)
+
+
 def test_ns5_in_place_zero_and_degenerate(torch_dev):
     torch, dev = torch_dev
     x = gauss(102, 0, (300, 200))
