@@ -112,6 +112,24 @@ def test_ns5_apply_on_one_round_of_big_tiles(torch_dev):
         assert err < NS_TOL, (i, err)
 
 
+def test_ns5_gram_on_one_round_of_big_tiles(torch_dev):
+    """Two [3072, 3072] matrices: their Gram and polynomial fit one round of 256-wide
+    tiles (78 upper tiles each, at most 20 per XCD) where 128-wide tiles would need two
+    (300 each, up to 76 per XCD), so both run on 256-wide tiles; one such matrix alone
+    (at most 10 and 38 per XCD) keeps 128-wide tiles. The outputs are equal bit for bit,
+    as both tiles accumulate over K in the same order, and match the oracle."""
+    torch, dev = torch_dev
+    shapes = [(3072, 3072)] * 2
+    xs = [gauss(105, i, s) for i, s in enumerate(shapes)]
+    outs = B.ns5_batched([to_dev(torch, dev, x) for x in xs])
+    alone = B.ns5_batched([to_dev(torch, dev, xs[1])])
+    torch.cuda.synchronize()
+    assert torch.equal(outs[1], alone[0])
+    err = rel_fro(to_host(outs[1]), O.newton_schulz(xs[1]))
+    log(f"  two [3072, 3072], matrix 1: rel err {err:.3e}")
+    assert err < NS_TOL, err
+
+
 def test_ns5_in_place_zero_and_degenerate(torch_dev):
     torch, dev = torch_dev
     x = gauss(102, 0, (300, 200))
