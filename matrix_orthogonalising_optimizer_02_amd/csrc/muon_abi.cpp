@@ -399,15 +399,19 @@ GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym, char* ws = nullpt
     GemmTile tile = (big_ok && big >= kGemmBigMinTiles) ? kTileBig : kTileSmall;
     // When a stage's big tiles fit in one round on every XCD while the small ones would
     // need more than one (two small blocks share a compute unit), and its tiles all have
-    // the same K (always for the polynomial and the Apply, whose K is m; for the Gram when
-    // every matrix has the same n), the big tile is faster. Measured: the H = 2048 block's
+    // the same K (the polynomial and the Apply, whose K is m, when every matrix of the
+    // group has the same m; the Gram when they have the same n), the big tile is faster. Measured: the H = 2048 block's
     // polynomial (180 big tiles) 0.080 -> 0.068 ms per launch; the Apply of one [4096,
     // 4096] matrix 0.166 -> 0.121 ms; with the Gram as well, ns5_batched on [4096, 4096]
     // 1.79 -> 1.51 ms, on [4096, 8192] 2.96 -> 2.44 ms. Both tiles accumulate over K in
     // the same order with the same epilogue arithmetic: the results are equal.
-    bool same_n = true;
-    for (int k = 1; k < ng; ++k) same_n = same_n && gp.mats[k].n_p == gp.mats[0].n_p;
-    if ((!sym || stage == kStagePoly || (stage == kStageGram && same_n)) && tile == kTileSmall && big_ok) {
+    bool same_m = true, same_n = true;
+    for (int k = 1; k < ng; ++k) {
+        same_m = same_m && gp.mats[k].m_p == gp.mats[0].m_p;
+        same_n = same_n && gp.mats[k].n_p == gp.mats[0].n_p;
+    }
+    const bool one_k = (sym && stage == kStageGram) ? same_n : same_m;
+    if (ng > 0 && one_k && tile == kTileSmall && big_ok) {
         int64_t cb[8] = {0}, cs[8] = {0};
         for (int k = 0; k < ng; ++k) {
             const int64_t tb = gp.mats[k].m_p / kGemmBigM, ts = gp.mats[k].m_p / kGemmSmall;
