@@ -148,6 +148,43 @@ int64_t big_tiles(const GroupPlan& gp, bool sym) {
     return big;
 }
 
+// The tile of a GEMM stage: big (256 x 256, one block per compute unit) when the stage
+// has at least kGemmBigMinTiles of them; also when its tiles all have the same K (the
+// polynomial and the Apply, whose K is m, when every matrix of the group has the same
+// m; the Gram when they have the same n) and the big tiles need fewer rounds on the
+// busiest XCD than the small ones (128 x 128, two blocks per compute unit); small
+// otherwise. Measured: ns5_batched on [4096, 4096] 1.79 -> 1.51 ms (Gram, polynomial
+// and Apply each one round of big tiles against two of small ones), on [6144, 6144]
+// 5.46 -> 4.36 ms (two rounds against three); the H = 2048 block's polynomial 0.080
+// -> 0.068 ms per launch. Both tiles accumulate over K in the same order with the same
+// epilogue arithmetic, so the choice alone changes no result.
+GemmTile choose_tile(const GroupPlan& gp, bool sym, int stage) {
+    const int ng = int(gp.mats.size());
+    const bool big_ok = !sym || kGemmBigM == kGemmBigN;
+    if (!big_ok || ng == 0) return kTileSmall;
+    if (big_tiles(gp, sym) >= kGemmBigMinTiles) return kTileBig;
+    bool same_m = true, same_n = true;
+    for (int k = 1; k < ng; ++k) {
+        same_m = same_m && gp.mats[k].m_p == gp.mats[0].m_p;
+        same_n = same_n && gp.mats[k].n_p == gp.mats[0].n_p;
+    }
+    if (!((sym && stage == kStageGram) ? same_n : same_m)) return kTileSmall;
+    int64_t cb[8] = {0}, cs[8] = {0};
+    for (int k = 0; k < ng; ++k) {
+        const int64_t tb = gp.mats[k].m_p / kGemmBigM, ts = gp.mats[k].m_p / kGemmSmall;
+        const int64_t Tb = sym ? tb * (tb + 1) / 2 : tb * (gp.mats[k].n_p / kGemmBigN);
+        const int64_t Ts = sym ? ts * (ts + 1) / 2 : ts * (gp.mats[k].n_p / kGemmSmall);
+        for (int x = 0; x < 8; ++x) {
+            cb[x] += ((x + 1) * Tb >> 3) - (x * Tb >> 3);
+            cs[x] += ((x + 1) * Ts >> 3) - (x * Ts >> 3);
+        }
+    }
+    const int64_t mb = *std::max_element(cb, cb + 8), ms = *std::max_element(cs, cs + 8);
+    const int64_t rounds_big = (mb + kCusPerXcd - 1) / kCusPerXcd;
+    const int64_t rounds_small = (ms + 2 * kCusPerXcd - 1) / (2 * kCusPerXcd);
+    return (mb > 0 && rounds_big < rounds_small) ? kTileBig : kTileSmall;
+}
+
 struct Plan {
     std::vector<GroupPlan> groups;
     size_t bytes = 0;
@@ -222,8 +259,7 @@ int make_plan(const int64_t* rows, const int64_t* cols, int32_t count, Plan* pla
             int64_t cnt[8];
             gp.tail_units = 0;
             for (int st = kStageGram; st <= kStageApply; ++st) {
-                const bool sym = st != kStageApply;
-                if ((sym && kGemmBigM != kGemmBigN) || big_tiles(gp, sym) < kGemmBigMinTiles) continue;
+                if (choose_tile(gp, st != kStageApply, st) != kTileBig) continue;
                 const int64_t ks = xcd_counts(gp, st, cnt);
                 if (ks) gp.tail_units = std::max(gp.tail_units, tail_split(cnt, ks, nullptr));
             }
@@ -385,46 +421,7 @@ struct IoPtrs {
 // tiles into the workspace's partial-tile region.
 GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym, char* ws = nullptr, int stage = kStageGram) {
     const int ng = int(gp.mats.size());
-    int64_t big = 0;
-    for (int k = 0; k < ng; ++k) {
-        const MatPlan& p = gp.mats[k];
-        if (sym) {
-            const int64_t t = p.m_p / kGemmBigM;
-            big += t * (t + 1) / 2;
-        } else {
-            big += (p.m_p / kGemmBigM) * (p.n_p / kGemmBigN);
-        }
-    }
-    const bool big_ok = !sym || kGemmBigM == kGemmBigN;
-    GemmTile tile = (big_ok && big >= kGemmBigMinTiles) ? kTileBig : kTileSmall;
-    // When a stage's big tiles fit in one round on every XCD while the small ones would
-    // need more than one (two small blocks share a compute unit), and its tiles all have
-    // the same K (the polynomial and the Apply, whose K is m, when every matrix of the
-    // group has the same m; the Gram when they have the same n), the big tile is faster. Measured: the H = 2048 block's
-    // polynomial (180 big tiles) 0.080 -> 0.068 ms per launch; the Apply of one [4096,
-    // 4096] matrix 0.166 -> 0.121 ms; with the Gram as well, ns5_batched on [4096, 4096]
-    // 1.79 -> 1.51 ms, on [4096, 8192] 2.96 -> 2.44 ms. Both tiles accumulate over K in
-    // the same order with the same epilogue arithmetic: the results are equal.
-    bool same_m = true, same_n = true;
-    for (int k = 1; k < ng; ++k) {
-        same_m = same_m && gp.mats[k].m_p == gp.mats[0].m_p;
-        same_n = same_n && gp.mats[k].n_p == gp.mats[0].n_p;
-    }
-    const bool one_k = (sym && stage == kStageGram) ? same_n : same_m;
-    if (ng > 0 && one_k && tile == kTileSmall && big_ok) {
-        int64_t cb[8] = {0}, cs[8] = {0};
-        for (int k = 0; k < ng; ++k) {
-            const int64_t tb = gp.mats[k].m_p / kGemmBigM, ts = gp.mats[k].m_p / kGemmSmall;
-            const int64_t Tb = sym ? tb * (tb + 1) / 2 : tb * (gp.mats[k].n_p / kGemmBigN);
-            const int64_t Ts = sym ? ts * (ts + 1) / 2 : ts * (gp.mats[k].n_p / kGemmSmall);
-            for (int x = 0; x < 8; ++x) {
-                cb[x] += ((x + 1) * Tb >> 3) - (x * Tb >> 3);
-                cs[x] += ((x + 1) * Ts >> 3) - (x * Ts >> 3);
-            }
-        }
-        const int64_t mb = *std::max_element(cb, cb + 8), ms = *std::max_element(cs, cs + 8);
-        if (mb > 0 && mb <= kCusPerXcd && ms > 2 * kCusPerXcd) tile = kTileBig;
-    }
+    const GemmTile tile = choose_tile(gp, sym, stage);
     const int64_t bm = tile == kTileBig ? kGemmBigM : kGemmSmall;
     const int64_t bn = tile == kTileBig ? kGemmBigN : kGemmSmall;
     for (int k = 0; k < ng; ++k) {

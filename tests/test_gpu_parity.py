@@ -112,21 +112,23 @@ def test_ns5_apply_on_one_round_of_big_tiles(torch_dev):
         assert err < NS_TOL, (i, err)
 
 
-def test_ns5_gram_on_one_round_of_big_tiles(torch_dev):
-    """Two [3072, 3072] matrices: their Gram and polynomial fit one round of 256-wide
-    tiles (78 upper tiles each, at most 20 per XCD) where 128-wide tiles would need two
-    (300 each, up to 76 per XCD), so both run on 256-wide tiles; one such matrix alone
-    (at most 10 and 38 per XCD) keeps 128-wide tiles. The outputs are equal bit for bit,
-    as both tiles accumulate over K in the same order, and match the oracle."""
+def test_ns5_stages_on_big_tiles_by_rounds(torch_dev):
+    """Five [2304, 2304] matrices: the Gram and polynomial need one round of 256-wide
+    tiles (25 to 30 upper tiles per XCD) against two of 128-wide ones (105 to 110), the
+    Apply two rounds (50 to 55 tiles) against four (200 to 205), so all three stages run
+    on 256-wide tiles; no XCD's last round is short enough to be split. One such matrix
+    alone (at most 6, 22, 11 and 41 tiles per XCD: one round either way) keeps 128-wide
+    tiles. The outputs are equal bit for bit, as both tiles accumulate over K in the same
+    order, and match the oracle."""
     torch, dev = torch_dev
-    shapes = [(3072, 3072)] * 2
+    shapes = [(2304, 2304)] * 5
     xs = [gauss(105, i, s) for i, s in enumerate(shapes)]
     outs = B.ns5_batched([to_dev(torch, dev, x) for x in xs])
-    alone = B.ns5_batched([to_dev(torch, dev, xs[1])])
+    alone = B.ns5_batched([to_dev(torch, dev, xs[4])])
     torch.cuda.synchronize()
-    assert torch.equal(outs[1], alone[0])
-    err = rel_fro(to_host(outs[1]), O.newton_schulz(xs[1]))
-    log(f"  two [3072, 3072], matrix 1: rel err {err:.3e}")
+    assert torch.equal(outs[4], alone[0])
+    err = rel_fro(to_host(outs[4]), O.newton_schulz(xs[4]))
+    log(f"  five [2304, 2304], matrix 4: rel err {err:.3e}")
     assert err < NS_TOL, err
 
 

@@ -14,7 +14,7 @@ Three sets exercise it:
     70 tiles and split their last 6 (all from matrix 9) in 5 chunks; in the Apply,
     XCDs 1, 3, 5 and 7 hold 130 tiles and split their last 2 (matrix 9) in 8 chunks;
   * [2048, 8448] and [8448, 2048]: the Gram and polynomial run on 128-wide tiles (72
-    big upper tiles), so the Apply also writes the row-major X'_r; every XCD holds 66
+    big upper tiles, one round either way), so the Apply also writes the row-major X'_r; every XCD holds 66
     Apply tiles and splits its last 2 (from the second matrix) in 8 chunks.
 The matrices with split tiles and the first one are checked against the float64
 oracle's Newton-Schulz at the bf16 tolerance, and each call is repeated to check
@@ -48,20 +48,28 @@ def log(msg):
     sys.stdout.flush()
 
 
+def xcd_counts(shapes, w, apply):
+    """Tiles of width w per XCD: each matrix's tiles dealt in contiguous eighths."""
+    cnt = [0] * 8
+    for a, b in shapes:
+        t = -(-min(a, b) // w)
+        T = t * (-(-max(a, b) // w)) if apply else t * (t + 1) // 2
+        for x in range(8):
+            cnt[x] += ((x + 1) * T >> 3) - (x * T >> 3)
+    return cnt
+
+
 def planned_split(shapes, apply=False):
     """XCD -> (tail tiles, chunks) by the library's rule, for a group whose matrices
     share the stage's K (m for the polynomial and Apply; these sets also share n where
-    the Gram splits). No split when the stage runs on 128-wide tiles."""
-    cnt = [0] * 8
-    big = 0
-    for a, b in shapes:
-        t = -(-min(a, b) // 256)
-        T = t * (-(-max(a, b) // 256)) if apply else t * (t + 1) // 2
-        big += T
-        for x in range(8):
-            cnt[x] += ((x + 1) * T >> 3) - (x * T >> 3)
-    if big < 512:
-        return {}
+    the Gram splits). No split when the stage runs on 128-wide tiles: it takes 256-wide
+    ones when they number at least 512, or when they need fewer rounds of the XCD's 32
+    compute units (one block each) than 128-wide tiles do (two blocks each)."""
+    cnt = xcd_counts(shapes, 256, apply)
+    if sum(cnt) < 512:
+        small = xcd_counts(shapes, 128, apply)
+        if not (max(cnt) > 0 and -(-max(cnt) // 32) < -(-max(small) // 64)):
+            return {}
     ksteps = -(-min(shapes[0]) // 256) * 256 // 32
     out = {}
     for x in range(8):
