@@ -15,7 +15,11 @@ Three sets exercise it:
     XCDs 1, 3, 5 and 7 hold 130 tiles and split their last 2 (matrix 9) in 8 chunks;
   * [2048, 8448] and [8448, 2048]: the Gram and polynomial run on 128-wide tiles (72
     big upper tiles, one round either way), so the Apply also writes the row-major X'_r; every XCD holds 66
-    Apply tiles and splits its last 2 (from the second matrix) in 8 chunks.
+    Apply tiles and splits its last 2 (from the second matrix) in 8 chunks;
+  * 2 x [4096, 4096]: only 272 upper tiles of 256, but two rounds of them per XCD (34
+    tiles) against three of 128-wide ones (132), so the Gram and polynomial run on
+    256-wide tiles and every XCD splits its last 2 (from the second matrix) in 8
+    chunks; the Apply (64 tiles per XCD) does not split.
 The matrices with split tiles and the first one are checked against the float64
 oracle's Newton-Schulz at the bf16 tolerance, and each call is repeated to check
 that the fixed-order chunk sums make it bitwise repeatable. The split itself is
@@ -40,6 +44,7 @@ CASES = [
     ([(2048, 2048)] * 16, [0, 12, 13, 14, 15], {1: (16, 2), 3: (16, 2), 5: (16, 2), 7: (16, 2)}, {}),
     ([(2560, 2560)] * 10, [0, 9], {x: (6, 5) for x in range(1, 8)}, {1: (2, 8), 3: (2, 8), 5: (2, 8), 7: (2, 8)}),
     ([(2048, 8448), (8448, 2048)], [0, 1], {}, {x: (2, 8) for x in range(8)}),
+    ([(4096, 4096)] * 2, [1], {x: (2, 8) for x in range(8)}, {}),
 ]
 
 
