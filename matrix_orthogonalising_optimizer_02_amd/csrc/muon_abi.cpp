@@ -138,7 +138,7 @@ int64_t xcd_counts(const GroupPlan& gp, int stage, int64_t cnt[8]) {
     return k > 0 ? k / 32 : 0;
 }
 
-// Big tiles of a stage: the rule that picks the big tile for it (see plan_tiles).
+// Big tiles of a stage, the first test of choose_tile.
 int64_t big_tiles(const GroupPlan& gp, bool sym) {
     int64_t big = 0;
     for (const MatPlan& p : gp.mats) {
@@ -154,9 +154,10 @@ int64_t big_tiles(const GroupPlan& gp, bool sym) {
 // m; the Gram when they have the same n) and the big tiles need fewer rounds on the
 // busiest XCD than the small ones (128 x 128, two blocks per compute unit); small
 // otherwise. Measured: ns5_batched on [4096, 4096] 1.79 -> 1.51 ms (Gram, polynomial
-// and Apply each one round of big tiles against two of small ones), on [6144, 6144]
-// 5.46 -> 4.36 ms (two rounds against three); the H = 2048 block's polynomial 0.080
-// -> 0.068 ms per launch. Both tiles accumulate over K in the same order with the same
+// and Apply each one round of big tiles against two of small ones); one [6144, 6144]
+// 5.20 -> 4.27 ms and two [4096, 4096] 3.34 -> 2.67 ms (the Gram and polynomial two
+// rounds against three, their short last round then split); the H = 2048 block's
+// polynomial 0.080 -> 0.068 ms per launch. Both tiles accumulate over K in the same order with the same
 // epilogue arithmetic, so the choice alone changes no result.
 GemmTile choose_tile(const GroupPlan& gp, bool sym, int stage) {
     const int ng = int(gp.mats.size());
@@ -415,8 +416,7 @@ struct IoPtrs {
 };
 
 // Fills tiles / tile_begin / total of a GEMM stage launch and returns the tile
-// configuration: the big tile when the stage has at least kGemmBigMinTiles of them
-// (symmetric stages need a square tile), the small one otherwise.
+// configuration that choose_tile picks for the stage.
 // ws != nullptr: the stage (Gram, polynomial or a non-final Apply) may split its tail
 // tiles into the workspace's partial-tile region.
 GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym, char* ws = nullptr, int stage = kStageGram) {
