@@ -131,6 +131,28 @@ void muon_default_hparams(muon_hparams* hp);
  * dims), TOO_LARGE. */
 int muon_workspace_bytes(const int64_t* rows, const int64_t* cols, int32_t count, size_t* bytes);
 
+/* The GEMM plan of the Newton-Schulz stages (Eq. 2 of the Muon scaling paper: the Gram
+ * X X^T, the polynomial b A + c A A, the Apply a X + B X) that ns5_batched and the
+ * refresh step of muon_step use for `count` matrices of shapes rows[i] x cols[i].
+ * Host only, touches no device; for tests and capacity planning. Nonempty matrices are
+ * grouped as those calls group them: sorted by m = min(rows, cols), then by
+ * n = max(rows, cols), both descending (stable), at most 16 per group. *groups receives
+ * the number of groups. With capacity >= groups * MUON_PLAN_RECORD_INTS, `out` (host
+ * array, caller-owned) receives one record of MUON_PLAN_RECORD_INTS values per group:
+ *   [0]        matrices in the group;
+ *   [1 .. 16]  their indices into rows / cols, -1 past that count;
+ *   then 17 values for each of the Gram, the polynomial, the Apply of iterations
+ *   1 .. N-1 and the last Apply, in that order: the tile width (128 or 256), then for
+ *   XCD 0 .. 7 the number of its last round's tiles that run as K chunks and the
+ *   number of chunks (0 and 1 where the XCD does not split).
+ * capacity 0 only reports *groups (out may then be NULL).
+ * Errors: INVALID_ARG (NULL groups, count < 0, NULL rows / cols with count > 0,
+ * negative dims, capacity < 0, NULL out with capacity > 0, capacity below the
+ * records), TOO_LARGE. */
+#define MUON_PLAN_RECORD_INTS 85
+int ns5_plan(const int64_t* rows, const int64_t* cols, int32_t count, int32_t* out, int32_t capacity,
+             int32_t* groups);
+
 /* One optimizer step at 0-based step index `step` for `count` matrices.
  * Periodic schedule (DiT paper, "NS5 once every K steps"; read here as a refresh
  * iff step % period_k == 0, so step 0 refreshes and period_k == 1 is vanilla Muon):

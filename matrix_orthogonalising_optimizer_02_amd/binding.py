@@ -31,7 +31,7 @@ KCLASS_NAMES = ("cast", "frob", "gram", "poly", "apply", "apply_final", "rownorm
                 "spec_bisect", "spec_entropy")
 
 EXPORTED = ("muon_abi_version", "muon_status_str", "muon_last_error", "muon_default_hparams",
-            "muon_workspace_bytes", "muon_step", "ns5_batched", "rownorm_update",
+            "muon_workspace_bytes", "ns5_plan", "muon_step", "ns5_batched", "rownorm_update",
             "adamw_default_hparams", "adamw_step", "svd_entropy_workspace_bytes", "svd_entropy",
             "rownorm_shard_workspace_bytes", "rownorm_shard_colsq", "rownorm_shard_apply",
             "muon_timing_enable", "muon_timing_read")
@@ -97,6 +97,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.muon_default_hparams.restype = None
     lib.muon_workspace_bytes.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64), i32,
                                          ctypes.POINTER(ctypes.c_size_t)]
+    lib.ns5_plan.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64), i32,
+                             ctypes.POINTER(ctypes.c_int32), i32, ctypes.POINTER(ctypes.c_int32)]
     lib.muon_step.argtypes = [ctypes.POINTER(MuonMatrix), i32, ctypes.POINTER(MuonHParams), i64, vp, sz, vp, vp]
     lib.ns5_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_int64),
                                 ctypes.POINTER(ctypes.c_int64), i32, ctypes.POINTER(MuonHParams), vp, sz, vp]
@@ -115,7 +117,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                         ctypes.POINTER(vp), vp, sz, vp]
     lib.muon_timing_enable.argtypes = [ctypes.c_int]
     lib.muon_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
-    for name in ("muon_step", "ns5_batched", "rownorm_update", "muon_workspace_bytes", "adamw_step",
+    for name in ("muon_step", "ns5_batched", "rownorm_update", "muon_workspace_bytes", "ns5_plan", "adamw_step",
                  "svd_entropy_workspace_bytes", "svd_entropy", "rownorm_shard_workspace_bytes",
                  "rownorm_shard_colsq", "rownorm_shard_apply", "muon_timing_enable", "muon_timing_read"):
         getattr(lib, name).restype = ctypes.c_int
@@ -151,6 +153,34 @@ def workspace_bytes(shapes: Sequence[Sequence[int]]) -> int:
     out = ctypes.c_size_t(0)
     _check(load_library().muon_workspace_bytes(rows, cols, n, ctypes.byref(out)), "muon_workspace_bytes")
     return int(out.value)
+
+
+PLAN_RECORD_INTS = 85
+PLAN_STAGES = ("gram", "poly", "apply", "apply_final")
+
+
+def ns5_plan(shapes: Sequence[Sequence[int]]):
+    """The Newton-Schulz GEMM plan the library uses for these shapes (host only): one
+    dict per group with the matrices' indices and, per stage, (tile width, {XCD: (tiles
+    of its last round run as K chunks, chunks)}) for the XCDs that split."""
+    lib = load_library()
+    n = len(shapes)
+    rows = (ctypes.c_int64 * max(n, 1))(*[int(s[0]) for s in shapes])
+    cols = (ctypes.c_int64 * max(n, 1))(*[int(s[1]) for s in shapes])
+    ng = ctypes.c_int32(0)
+    _check(lib.ns5_plan(rows, cols, n, None, 0, ctypes.byref(ng)), "ns5_plan")
+    cap = max(ng.value, 1) * PLAN_RECORD_INTS
+    out = (ctypes.c_int32 * cap)()
+    _check(lib.ns5_plan(rows, cols, n, out, cap, ctypes.byref(ng)), "ns5_plan")
+    groups = []
+    for g in range(ng.value):
+        r = out[g * PLAN_RECORD_INTS:(g + 1) * PLAN_RECORD_INTS]
+        rec = {"indices": [int(v) for v in r[1:1 + r[0]]]}
+        for st, name in enumerate(PLAN_STAGES):
+            q = r[17 + 17 * st:34 + 17 * st]
+            rec[name] = (int(q[0]), {x: (int(q[1 + 2 * x]), int(q[2 + 2 * x])) for x in range(8) if q[1 + 2 * x] > 0})
+        groups.append(rec)
+    return groups
 
 
 # ------------------------------------------------------------ tensor helpers ----

@@ -418,8 +418,10 @@ struct IoPtrs {
 // Fills tiles / tile_begin / total of a GEMM stage launch and returns the tile
 // configuration that choose_tile picks for the stage.
 // ws != nullptr: the stage (Gram, polynomial or a non-final Apply) may split its tail
-// tiles into the workspace's partial-tile region.
-GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym, char* ws = nullptr, int stage = kStageGram) {
+// tiles into the workspace's partial-tile region. describe: plan that split without a
+// workspace (ns5_plan reads xtail / xsplit; na.tail stays NULL).
+GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym, char* ws = nullptr, int stage = kStageGram,
+                    bool describe = false) {
     const int ng = int(gp.mats.size());
     const GemmTile tile = choose_tile(gp, sym, stage);
     const int64_t bm = tile == kTileBig ? kGemmBigM : kGemmSmall;
@@ -449,7 +451,7 @@ GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym, char* ws = nullpt
     na.total = int32_t(tot);
     na.tail = nullptr;
     na.fix_total = 0;
-    if (tile == kTileBig && ws != nullptr && gp.tail_units > 0) {
+    if (tile == kTileBig && (ws != nullptr || describe) && gp.tail_units > 0) {
         int64_t cnt[8], fix = 0, longest = 0;
         const int64_t ks = xcd_counts(gp, stage, cnt);
         const int64_t units = ks ? tail_split(cnt, ks, &na) : 0;
@@ -458,7 +460,7 @@ GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym, char* ws = nullpt
                 fix += na.xtail[x];
                 longest = std::max<int64_t>(longest, int64_t(na.xfull[x]) + int64_t(na.xtail[x]) * na.xsplit[x]);
             }
-            na.tail = reinterpret_cast<float*>(ws + gp.tail);
+            na.tail = ws ? reinterpret_cast<float*>(ws + gp.tail) : nullptr;
             na.fix_total = int32_t(fix);
             na.total = int32_t(8 * longest);
         }
@@ -993,6 +995,45 @@ MUON_API int muon_workspace_bytes(const int64_t* rows, const int64_t* cols, int3
     const int rc = make_plan(rows, cols, count, &plan);
     if (rc) return rc;
     *bytes = plan.bytes;
+    return MUON_OK;
+}
+
+MUON_API int ns5_plan(const int64_t* rows, const int64_t* cols, int32_t count, int32_t* out, int32_t capacity,
+                      int32_t* groups) {
+    g_last_error.clear();
+    if (!groups) return fail(MUON_ERR_INVALID_ARG, "groups is NULL");
+    if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count < 0");
+    if (count > 0 && (!rows || !cols)) return fail(MUON_ERR_INVALID_ARG, "rows or cols is NULL");
+    if (capacity < 0 || (capacity > 0 && !out)) return fail(MUON_ERR_INVALID_ARG, "out is NULL or capacity < 0");
+    Plan plan;
+    const int rc = make_plan(rows, cols, count, &plan);
+    if (rc) return rc;
+    const int64_t ng = int64_t(plan.groups.size());
+    *groups = int32_t(ng);
+    if (capacity == 0) return MUON_OK;
+    if (ng * MUON_PLAN_RECORD_INTS > capacity)
+        return fail(MUON_ERR_INVALID_ARG, "capacity holds fewer than groups x MUON_PLAN_RECORD_INTS values");
+    static_assert(MUON_PLAN_RECORD_INTS == 1 + kMaxGroup + 4 * 17, "plan record layout");
+    for (int64_t g = 0; g < ng; ++g) {
+        const GroupPlan& gp = plan.groups[size_t(g)];
+        int32_t* r = out + g * MUON_PLAN_RECORD_INTS;
+        r[0] = int32_t(gp.mats.size());
+        for (int k = 0; k < kMaxGroup; ++k) r[1 + k] = k < int(gp.mats.size()) ? int32_t(gp.mats[size_t(k)].idx) : -1;
+        // Gram, polynomial, Apply of iterations 1..N-1, last Apply: as run_refresh plans them
+        const bool sym[4] = {true, true, false, false};
+        const int stage[4] = {kStageGram, kStagePoly, kStageApply, kStageApply};
+        const bool split[4] = {true, true, true, false};
+        for (int st = 0; st < 4; ++st) {
+            NsArgs na{};
+            const GemmTile tile = plan_tiles(gp, na, sym[st], nullptr, stage[st], split[st]);
+            int32_t* q = r + 1 + kMaxGroup + st * 17;
+            q[0] = tile == kTileBig ? int32_t(kGemmBigM) : int32_t(kGemmSmall);
+            for (int x = 0; x < 8; ++x) {
+                q[1 + 2 * x] = na.fix_total > 0 ? na.xtail[x] : 0;
+                q[2 + 2 * x] = na.fix_total > 0 ? na.xsplit[x] : 1;
+            }
+        }
+    }
     return MUON_OK;
 }
 

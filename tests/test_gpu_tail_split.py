@@ -5,8 +5,8 @@ every matrix of the group has the same K for it, an XCD whose tile count leaves 
 round of at most 16 tiles (of its 32 compute units) runs those tiles as K chunks that
 write fp32 partial tiles; a fixup launch adds each tile's chunks in chunk order and
 applies the stage's epilogue. The split is taken only when the modelled time it saves
-exceeds the cost of its partial tiles (the library's planning rule, mirrored below).
-Three sets exercise it:
+exceeds the cost of its partial tiles (the library's planning rule).
+Four sets exercise it:
   * 16 x [2048, 2048] (576 upper tiles): in the Gram and polynomial, XCDs 1, 3, 5 and
     7 hold 80 tiles and split their last 16 (from matrices 12 to 15) in 2 chunks; the
     Apply (128 tiles per XCD) does not split;
@@ -22,9 +22,9 @@ Three sets exercise it:
     chunks; the Apply (64 tiles per XCD) does not split.
 The matrices with split tiles and the first one are checked against the float64
 oracle's Newton-Schulz at the bf16 tolerance, and each call is repeated to check
-that the fixed-order chunk sums make it bitwise repeatable. The split itself is
-recomputed here from the planning rule, so a change of rule that stops exercising
-it fails the test.
+that the fixed-order chunk sums make it bitwise repeatable. The library's plan
+(ns5_plan) must be the split listed here, so a change of rule that stops exercising
+it fails the test; the rule itself is checked on the CPU over many sets.
 """
 import sys
 
@@ -53,43 +53,6 @@ def log(msg):
     sys.stdout.flush()
 
 
-def xcd_counts(shapes, w, apply):
-    """Tiles of width w per XCD: each matrix's tiles dealt in contiguous eighths."""
-    cnt = [0] * 8
-    for a, b in shapes:
-        t = -(-min(a, b) // w)
-        T = t * (-(-max(a, b) // w)) if apply else t * (t + 1) // 2
-        for x in range(8):
-            cnt[x] += ((x + 1) * T >> 3) - (x * T >> 3)
-    return cnt
-
-
-def planned_split(shapes, apply=False):
-    """XCD -> (tail tiles, chunks) by the library's rule, for a group whose matrices
-    share the stage's K (m for the polynomial and Apply; these sets also share n where
-    the Gram splits). No split when the stage runs on 128-wide tiles: it takes 256-wide
-    ones when they number at least 512, or when they need fewer rounds of the XCD's 32
-    compute units (one block each) than 128-wide tiles do (two blocks each)."""
-    cnt = xcd_counts(shapes, 256, apply)
-    if sum(cnt) < 512:
-        small = xcd_counts(shapes, 128, apply)
-        if not (max(cnt) > 0 and -(-max(cnt) // 32) < -(-max(small) // 64)):
-            return {}
-    ksteps = -(-min(shapes[0]) // 256) * 256 // 32
-    out = {}
-    for x in range(8):
-        r = cnt[x] % 32
-        S = min(8, 32 // r, ksteps // 8) if 0 < r <= 16 else 1
-        if S >= 2:
-            out[x] = (r, S)
-    if not out:
-        return out
-    units = sum(r * S for r, S in out.values())
-    s_min = min(S for _, S in out.values())
-    saved = (1.0 - 1.0 / s_min) * ksteps * 0.86
-    return out if saved > units * 0.13 + 10.0 else {}
-
-
 @pytest.fixture(scope="module")
 def torch_dev():
     import torch
@@ -102,8 +65,10 @@ def torch_dev():
 def test_split_tail_tiles_vs_oracle_and_repeatable(torch_dev, case):
     torch, dev = torch_dev
     shapes, checked, split, split_apply = CASES[case]
-    assert planned_split(shapes) == split
-    assert planned_split(shapes, apply=True) == split_apply
+    plan = B.ns5_plan(shapes)
+    assert len(plan) == 1 and plan[0]["apply"][0] == 256
+    assert plan[0]["gram"][1] == plan[0]["poly"][1] == split
+    assert plan[0]["apply"][1] == split_apply and plan[0]["apply_final"][1] == {}
     xs = [WL.host_normal(7 + case, WL.ROLE_G, i, s, 1e-3) for i, s in enumerate(shapes)]
     ins = [torch.from_numpy(x.astype(np.float32)).to(dev) for x in xs]
     log(f"ns5_batched: {shapes}, split tail tiles {split}, Apply {split_apply}")

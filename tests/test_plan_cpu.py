@@ -1,0 +1,167 @@
+"""Host-side planning of the Newton-Schulz GEMM stages, checked on the CPU.
+
+The library's own plan (the host-only ns5_plan query, which runs the code the launches
+run) is compared with the planning rules as stated here, written independently of the
+library's C++:
+  * grouping: nonempty matrices, working shape m = min(rows, cols), n = max(rows, cols),
+    each padded up to a multiple of 256; a stable sort by (m, n), both descending;
+    groups of at most 16;
+  * tiles: the Gram and polynomial count the upper triangle of a [m, m] tile grid
+    (diagonal included), the Apply every tile of [m, n]; each of the 8 XCDs takes a
+    contiguous eighth of every matrix's tiles;
+  * tile width per stage: 256 when the stage has at least 512 such tiles; otherwise,
+    when every matrix of the group has the same K for the stage (n for the Gram, m for
+    the polynomial and the Apply), 256 when the busiest XCD needs fewer rounds of them
+    (32 per round, one block per compute unit) than of 128-wide tiles (64 per round, two
+    blocks per compute unit); 128 otherwise;
+  * tail split, for a stage on 256-wide tiles whose matrices share K: an XCD whose last
+    round holds r <= 16 tiles runs them as S = min(8, 32 // r, K / 256) chunks of K
+    (S >= 2), taken only when (1 - 1 / S_min) of a tile's K steps at 0.86 us each exceeds
+    0.13 us per partial tile plus 10 us; the partial-tile region is sized for the stage
+    that splits the most tiles, and the last Apply never splits.
+Sets: the benchmark workloads, the GPU tests' sets, and a seeded sweep of random sets.
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+from matrix_orthogonalising_optimizer_02_amd import binding as B
+from matrix_orthogonalising_optimizer_02_amd import workloads as WL
+
+PAD, GROUP, XCDS, CUS = 256, 16, 8, 32
+
+
+def _lib_or_skip():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libmuon_rocm.so is not built")
+    return B.load_library()
+
+
+def ceil_div(a, b):
+    return -(-a // b)
+
+
+def eighths(total):
+    return [((x + 1) * total >> 3) - (x * total >> 3) for x in range(XCDS)]
+
+
+def per_xcd(mats, stage, width):
+    cnt = [0] * XCDS
+    for m, n in mats:
+        t = m // width
+        total = t * (n // width) if stage == "apply" else t * (t + 1) // 2
+        cnt = [c + e for c, e in zip(cnt, eighths(total))]
+    return cnt
+
+
+def shared_k(mats, stage):
+    ks = {n if stage == "gram" else m for m, n in mats}
+    return ks.pop() if len(ks) == 1 else None
+
+
+def tile_width(mats, stage):
+    big = per_xcd(mats, stage, 256)
+    if sum(big) >= 512:
+        return 256
+    if shared_k(mats, stage) is None:
+        return 128
+    small = per_xcd(mats, stage, 128)
+    return 256 if max(big) > 0 and ceil_div(max(big), CUS) < ceil_div(max(small), 2 * CUS) else 128
+
+
+def tail_split(mats, stage):
+    """(partial tiles, {XCD: (tail tiles, chunks)}) of a stage on 256-wide tiles."""
+    k = shared_k(mats, stage)
+    if k is None:
+        return 0, {}
+    ksteps = k // 32
+    out = {}
+    for x, c in enumerate(per_xcd(mats, stage, 256)):
+        r = c % CUS
+        if 0 < r <= CUS // 2:
+            s = min(8, CUS // r, ksteps // 8)
+            if s >= 2:
+                out[x] = (r, s)
+    if not out:
+        return 0, {}
+    units = sum(r * s for r, s in out.values())
+    s_min = min(s for _, s in out.values())
+    if (1.0 - 1.0 / s_min) * ksteps * 0.86 <= units * 0.13 + 10.0:
+        return 0, {}
+    return units, out
+
+
+def expected_plan(shapes):
+    work = []
+    for i, (a, b) in enumerate(shapes):
+        if a == 0 or b == 0:
+            continue
+        work.append((ceil_div(min(a, b), PAD) * PAD, ceil_div(max(a, b), PAD) * PAD, min(a, b), max(a, b), i))
+    work.sort(key=lambda w: (-w[2], -w[3]))  # stable: equal shapes keep their order
+    groups = []
+    for g0 in range(0, len(work), GROUP):
+        grp = work[g0:g0 + GROUP]
+        mats = [(w[0], w[1]) for w in grp]
+        tiles = {st: tile_width(mats, st) for st in ("gram", "poly", "apply")}
+        splits = {st: tail_split(mats, st) if tiles[st] == 256 else (0, {}) for st in tiles}
+        rec = {"indices": [w[4] for w in grp]}
+        for st in ("gram", "poly", "apply"):
+            rec[st] = (tiles[st], splits[st][1])
+        rec["apply_final"] = (tiles["apply"], {})
+        groups.append(rec)
+    return groups
+
+
+def bench_and_test_sets():
+    sets = [list(wl.shapes) for wl in WL.WORKLOADS]
+    sets += [
+        [(2048, 2048)] * 16, [(2560, 2560)] * 10, [(2048, 8448), (8448, 2048)], [(4096, 4096)] * 2,
+        [(2304, 2304)] * 5, [(2304, 2304)], [(2048, 2048)] * 3, [(3072, 3072)] * 2, [(6144, 6144)],
+        [(2048, 8192)] * 20, [(0, 5), (300, 70), (7, 0), (70, 300)],
+    ]
+    return sets
+
+
+@pytest.mark.parametrize("case", range(len(bench_and_test_sets())))
+def test_plan_of_bench_and_test_sets(case):
+    _lib_or_skip()
+    shapes = bench_and_test_sets()[case]
+    assert B.ns5_plan(shapes) == expected_plan(shapes)
+
+
+def test_plan_of_random_sets():
+    """Seeded random sets: sizes around the tile and padding edges, 1 to 40 matrices,
+    shapes repeated so that groups often share K."""
+    _lib_or_skip()
+    rng = np.random.default_rng(20240607)
+    sizes = [1, 100, 128, 255, 256, 257, 512, 1000, 1536, 2048, 2304, 2560, 3072, 3840, 4096, 5120, 6144, 8192]
+    splits = 0
+    for trial in range(300):
+        kinds = int(rng.integers(1, 4))
+        pool = [(int(rng.choice(sizes)), int(rng.choice(sizes))) for _ in range(kinds)]
+        shapes = [pool[int(rng.integers(0, kinds))] for _ in range(int(rng.integers(1, 41)))]
+        want = expected_plan(shapes)
+        assert B.ns5_plan(shapes) == want, (trial, shapes)
+        splits += sum(1 for g in want for st in ("gram", "poly", "apply") if g[st][1])
+    assert splits > 20  # the sweep exercises the split rule, not only the tile rule
+
+
+def test_plan_argument_errors():
+    lib = _lib_or_skip()
+    rows = (ctypes.c_int64 * 2)(64, 128)
+    cols = (ctypes.c_int64 * 2)(64, 256)
+    ng = ctypes.c_int32(-1)
+    assert lib.ns5_plan(rows, cols, 2, None, 0, None) == B.MUON_ERR_INVALID_ARG
+    assert lib.ns5_plan(rows, cols, -1, None, 0, ctypes.byref(ng)) == B.MUON_ERR_INVALID_ARG
+    assert lib.ns5_plan(None, None, 1, None, 0, ctypes.byref(ng)) == B.MUON_ERR_INVALID_ARG
+    assert lib.ns5_plan(rows, cols, 2, None, 5, ctypes.byref(ng)) == B.MUON_ERR_INVALID_ARG
+    short = (ctypes.c_int32 * (B.PLAN_RECORD_INTS - 1))()
+    assert lib.ns5_plan(rows, cols, 2, short, B.PLAN_RECORD_INTS - 1, ctypes.byref(ng)) == B.MUON_ERR_INVALID_ARG
+    assert lib.ns5_plan(rows, cols, 2, None, 0, ctypes.byref(ng)) == B.MUON_OK and ng.value == 1
+    assert lib.ns5_plan(None, None, 0, None, 0, ctypes.byref(ng)) == B.MUON_OK and ng.value == 0
+    bad = (ctypes.c_int64 * 1)(1 << 31)
+    assert lib.ns5_plan(bad, cols, 1, None, 0, ctypes.byref(ng)) == B.MUON_ERR_TOO_LARGE
+    neg = (ctypes.c_int64 * 1)(-3)
+    assert lib.ns5_plan(neg, cols, 1, None, 0, ctypes.byref(ng)) == B.MUON_ERR_INVALID_ARG
