@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     make_workspace,
     muon_step,
     ns5_batched,
+    ns5_plan,
     rownorm_shard_apply,
     rownorm_shard_colsq,
     rownorm_shard_workspace_bytes,
