@@ -597,10 +597,12 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
     // (16 lanes per row, 4 rows per 1 KiB DMA load) instead of 32 rows x 8 bytes per
     // instruction. Chunk c of row r is stored at position c ^ (r & 15). The block sits
     // over the direct-staging area: it is read into registers before any staging write,
-    // and x_dma waits until earlier LDS reads of the area are done. (The final Apply
-    // keeps direct loads: its wait for the block would also wait for the first half's
-    // W stores.)
-    constexpr bool kDmaX = (MODE == kModePoly || MODE == kModeApply) && Cfg::kDirect && WM == 128 && HN == 64;
+    // and x_dma waits until earlier LDS reads of the area are done. The Apply with the
+    // fused update takes this path for its first half only: for the second, the wait
+    // for the block would also wait for the first half's W stores, so it keeps direct
+    // loads (measured: 16 x [2048, 8192] last Apply 1.58-1.64 -> 1.55 ms, spills 30 -> 2).
+    constexpr bool kDmaX = (MODE == kModePoly || MODE == kModeApply || MODE == kModeFinalW) && Cfg::kDirect &&
+                           WM == 128 && HN == 64;
     unsigned short* const xs = sA + __builtin_amdgcn_readfirstlane(wave) * (Cfg::kEpiWave / 2) + HN * TSB;
     auto x_dma = [&](int hh) {
         const unsigned short* src = (MODE == kModePoly) ? d.a : d.xc;
@@ -632,7 +634,7 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         // operands of the epilogue math for this half: 8 contiguous bytes per (a, b, rg)
         u32x2 opv[TM][NBH][4];
         if constexpr (MODE != kModeGram) {
-            if constexpr (kDmaX) {
+            if (kDmaX && (MODE != kModeFinalW || h == 0)) {
                 x_dma(h);
                 wait_vmcnt<0>();
                 x_read(opv);
