@@ -148,6 +148,13 @@ def test_plan_of_random_sets():
     assert splits > 20  # the sweep exercises the split rule, not only the tile rule
 
 
+def test_record_size_matches_the_header():
+    import re
+    text = open(B.HEADER).read()
+    m = re.search(r"#define MUON_PLAN_RECORD_INTS (\d+)", text)
+    assert m and int(m.group(1)) == B.PLAN_RECORD_INTS == 1 + GROUP + 4 * 17
+
+
 def test_plan_argument_errors():
     lib = _lib_or_skip()
     rows = (ctypes.c_int64 * 2)(64, 128)
