@@ -150,7 +150,8 @@ def test_plan_of_random_sets():
 
 def test_record_size_matches_the_header():
     import re
-    text = open(B.HEADER).read()
+    header = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "muon_rocm.h")
+    text = open(header).read()
     m = re.search(r"#define MUON_PLAN_RECORD_INTS (\d+)", text)
     assert m and int(m.group(1)) == B.PLAN_RECORD_INTS == 1 + GROUP + 4 * 17
 
