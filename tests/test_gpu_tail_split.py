@@ -24,7 +24,10 @@ The matrices with split tiles and the first one are checked against the float64
 oracle's Newton-Schulz at the bf16 tolerance, and each call is repeated to check
 that the fixed-order chunk sums make it bitwise repeatable. The library's plan
 (ns5_plan) must be the split listed here, so a change of rule that stops exercising
-it fails the test; the rule itself is checked on the CPU over many sets.
+it fails the test; the rule itself is checked on the CPU over many sets. A seeded
+sweep of six further sets (sides 2048 to 3072, one or two shapes, up to 16 matrices,
+kept when the plan splits a tail or takes 256-wide tiles below 512 of them) checks the
+first and last matrix of each against the oracle and every output for repeatability.
 """
 import sys
 
@@ -77,6 +80,60 @@ def test_split_tail_tiles_vs_oracle_and_repeatable(torch_dev, case):
     torch.cuda.synchronize()
     for i, (o, o2) in enumerate(zip(outs, outs2)):
         assert torch.equal(o, o2), f"matrix {i}: two calls differ"
+    for i in checked:
+        ref = O.newton_schulz(xs[i].astype(np.float32).astype(np.float64))
+        oh = outs[i].detach().cpu().numpy().astype(np.float64)
+        err = float(np.linalg.norm(oh - ref) / np.linalg.norm(ref))
+        log(f"  matrix {i} {shapes[i]}: rel err {err:.3e}")
+        assert err < NS_TOL, (i, err)
+
+
+def random_big_sets(count=6, seed=20241202):
+    """Seeded sets on 256-wide tiles: m from 2048 to 3072, n = m, m + 256 or 2 m, random
+    orientation, 1 to 16 matrices of one or two shapes; a set is kept when the library's
+    plan splits a tail in some stage or takes 256-wide tiles for a stage with fewer than
+    512 of them (the fewer-rounds rule)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        kinds = int(rng.integers(1, 3))
+        m = int(rng.choice([2048, 2304, 2560, 2816, 3072]))
+        pool = []
+        for _ in range(kinds):
+            n = int(rng.choice([m, m + 256, 2 * m]))
+            pool.append((m, n) if rng.random() < 0.5 else (n, m))
+        shapes = [pool[int(rng.integers(0, kinds))] for _ in range(int(rng.integers(1, 17)))]
+        plan = B.ns5_plan(shapes)
+        split = any(g[st][1] for g in plan for st in ("gram", "poly", "apply"))
+        few = False
+        for g in plan:
+            mats = [(min(shapes[i]), max(shapes[i])) for i in g["indices"]]
+            ms = [(-(-a // 256), -(-b // 256)) for a, b in mats]
+            if g["gram"][0] == 256 and sum(t * (t + 1) // 2 for t, _ in ms) < 512:
+                few = True
+            if g["apply"][0] == 256 and sum(t * u for t, u in ms) < 512:
+                few = True
+        if split or few:
+            out.append((shapes, split, few))
+    return out
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_big_sets_vs_oracle(torch_dev, case):
+    torch, dev = torch_dev
+    sets = random_big_sets()
+    assert sum(1 for _, s, _ in sets if s) >= 3 and sum(1 for _, _, f in sets if f) >= 1
+    shapes, split, few = sets[case]
+    plan = B.ns5_plan(shapes)
+    xs = [WL.host_normal(31 + case, WL.ROLE_G, i, s, 1e-3) for i, s in enumerate(shapes)]
+    ins = [torch.from_numpy(x.astype(np.float32)).to(dev) for x in xs]
+    log(f"ns5_batched: {len(shapes)} matrices {sorted(set(shapes))}, split {split}, fewer-rounds tiles {few}")
+    outs = B.ns5_batched(ins)
+    outs2 = B.ns5_batched(ins)
+    torch.cuda.synchronize()
+    for i, (o, o2) in enumerate(zip(outs, outs2)):
+        assert torch.equal(o, o2), f"matrix {i}: two calls differ"
+    checked = sorted({plan[0]["indices"][0], plan[-1]["indices"][-1]})
     for i in checked:
         ref = O.newton_schulz(xs[i].astype(np.float32).astype(np.float64))
         oh = outs[i].detach().cpu().numpy().astype(np.float64)
