@@ -13,6 +13,5 @@ from .muon_oracle import (  # noqa: F401
     row_normalise,
     rownorm_step,
     rownorm_update_direction,
-    scaled_update,
     vanilla_step,
 )

@@ -132,13 +132,6 @@ def row_normalise(m, eps: float = 1e-7) -> np.ndarray:
     return x / np.maximum(norms, eps)
 
 
-def scaled_update(w, u, lr: float, weight_decay: float, rms_scale: float = 0.2) -> np.ndarray:
-    """W_t = W_{t-1} - lr * (0.2 * U * sqrt(max(A, B)) + lambda * W_{t-1}) ([MS] Eq. 4, R7)."""
-    w = _f64(w)
-    n = max(w.shape)
-    return w - lr * (rms_scale * _f64(u) * math.sqrt(n) + weight_decay * w)
-
-
 def rms(x) -> float:
     """RMS(X) = sqrt(mean of the squared entries) ([MS] Lemma 1, Sec. 3.1 Eq. 6)."""
     x = _f64(x)
