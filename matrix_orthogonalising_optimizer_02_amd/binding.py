@@ -213,10 +213,35 @@ def make_workspace(shapes, device="cuda"):
     return torch.empty(max(workspace_bytes(shapes), 1), dtype=torch.uint8, device=device)
 
 
-def _ws(workspace, shapes, device):
+def _torch_stream(stream, device):
+    """The torch stream object for `stream` (None: the device's current stream)."""
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(getattr(stream, "cuda_stream", stream)), device=device)
+
+
+def _scratch(nbytes, device, stream):
+    """A device buffer for one library call, allocated on the stream the call enqueues on.
+
+    torch's caching allocator keeps a freed block with the stream it was allocated on
+    and hands it out again only to allocations on that stream, which run after the
+    call's kernels in stream order. A buffer allocated on another stream could be
+    reused there while the call's kernels still write it.
+    """
+    torch = _torch()
+    with torch.cuda.stream(_torch_stream(stream, device)):
+        return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _ws(workspace, shapes, device, stream):
+    """(pointer, size, owner) of the call's workspace; `owner` must stay referenced until
+    the library call has returned."""
     if workspace is None:
-        workspace = make_workspace(shapes, device)
-    return ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel())
+        workspace = _scratch(workspace_bytes(shapes), device, stream)
+    return ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()), workspace
 
 
 def _matrices(weights, momenta, grads):
@@ -256,7 +281,7 @@ def muon_step(weights, momenta, grads, step: int, hp: Optional[MuonHParams] = No
     hp = hp or default_hparams()
     arr = _matrices(weights, momenta, grads)
     dev = weights[0].device if weights else None
-    ws, wsb = _ws(workspace, [tuple(w.shape) for w in weights], dev)
+    ws, wsb, _owner = _ws(workspace, [tuple(w.shape) for w in weights], dev, stream)
     rc = load_library().muon_step(arr, len(weights), ctypes.byref(hp), int(step), ws, wsb,
                                   _monitor_ptr(update_rms, len(weights)), _stream_handle(stream, dev))
     _check(rc, "muon_step")
@@ -268,7 +293,7 @@ def rownorm_update(weights, momenta, grads, hp: Optional[MuonHParams] = None, wo
     hp = hp or default_hparams()
     arr = _matrices(weights, momenta, grads)
     dev = weights[0].device if weights else None
-    ws, wsb = _ws(workspace, [tuple(w.shape) for w in weights], dev)
+    ws, wsb, _owner = _ws(workspace, [tuple(w.shape) for w in weights], dev, stream)
     rc = load_library().rownorm_update(arr, len(weights), ctypes.byref(hp), ws, wsb,
                                        _monitor_ptr(update_rms, len(weights)), _stream_handle(stream, dev))
     _check(rc, "rownorm_update")
@@ -296,7 +321,7 @@ def ns5_batched(inputs, outputs=None, hp: Optional[MuonHParams] = None, workspac
         outs[i] = o.data_ptr() or None
         rows[i], cols[i] = x.shape
     dev = inputs[0].device if inputs else None
-    ws, wsb = _ws(workspace, [tuple(x.shape) for x in inputs], dev)
+    ws, wsb, _owner = _ws(workspace, [tuple(x.shape) for x in inputs], dev, stream)
     rc = load_library().ns5_batched(ins, outs, rows, cols, n, ctypes.byref(hp), ws, wsb,
                                     _stream_handle(stream, dev))
     _check(rc, "ns5_batched")
@@ -400,12 +425,12 @@ def rownorm_shard_workspace_bytes(shapes, full_rows) -> int:
     return int(out.value)
 
 
-def _shard_ws(workspace, weights, full_rows, dev):
+def _shard_ws(workspace, weights, full_rows, dev, stream):
+    """As _ws, for the shard calls."""
     if workspace is None:
-        torch = _torch()
         nb = rownorm_shard_workspace_bytes([tuple(w.shape) for w in weights], full_rows)
-        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
-    return ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel())
+        workspace = _scratch(nb, dev, stream)
+    return ctypes.c_void_p(workspace.data_ptr()), ctypes.c_size_t(workspace.numel()), workspace
 
 
 def _sum_ptrs(tensors, weights, name):
@@ -431,7 +456,7 @@ def rownorm_shard_colsq(weights, momenta, grads, full_rows, colsq=None, hp: Opti
     if colsq is None:
         colsq = [torch.empty(w.shape[1], dtype=torch.float32, device=dev) for w in weights]
     arr = _shards(weights, momenta, grads, full_rows)
-    ws, wsb = _shard_ws(workspace, weights, full_rows, dev)
+    ws, wsb, _owner = _shard_ws(workspace, weights, full_rows, dev, stream)
     rc = load_library().rownorm_shard_colsq(arr, len(weights), ctypes.byref(hp), _sum_ptrs(colsq, weights, "colsq"),
                                             ws, wsb, _stream_handle(stream, dev))
     _check(rc, "rownorm_shard_colsq")
@@ -444,7 +469,7 @@ def rownorm_shard_apply(weights, momenta, full_rows, colsq_total, hp: Optional[M
     hp = hp or default_hparams()
     dev = weights[0].device if weights else None
     arr = _shards(weights, momenta, None, full_rows)
-    ws, wsb = _shard_ws(workspace, weights, full_rows, dev)
+    ws, wsb, _owner = _shard_ws(workspace, weights, full_rows, dev, stream)
     rc = load_library().rownorm_shard_apply(arr, len(weights), ctypes.byref(hp),
                                             _sum_ptrs(colsq_total, weights, "colsq_total"), ws, wsb,
                                             _stream_handle(stream, dev))
@@ -499,7 +524,7 @@ def svd_entropy(weights, entropy=None, sigma_sq=None, workspace=None, stream=Non
     ptrs = (ctypes.c_void_p * max(n, 1))(*[w.data_ptr() or None for w in weights])
     rows, cols = _shape_arrays(shapes)
     if workspace is None:
-        workspace = make_svd_entropy_workspace(shapes, dev)
+        workspace = _scratch(svd_entropy_workspace_bytes(shapes), dev, stream)
     rc = load_library().svd_entropy(ptrs, rows, cols, n, ctypes.c_void_p(workspace.data_ptr()),
                                     ctypes.c_size_t(workspace.numel()),
                                     ctypes.c_void_p(entropy.data_ptr() or None),
