@@ -7,7 +7,10 @@ checked on outputs it can compute piece by piece:
   * a RowNorm step on sampled rows of flat matrices and sampled columns of tall
     ones (each depends only on its own row or column), at 1e-5;
   * a refresh step (W = 0 probe) on whole sampled matrices, the smallest of the
-    workload and one tall one, against the oracle's NS5, at 2e-2;
+    workload and one tall one, and for the 15B-scale set also its largest tall
+    [30720, 5120] and flat [5120, 20480] matrices, against the oracle's NS5, at 2e-2
+    for the whole matrix and 6e-2 for every row of a flat output (column of a tall
+    one), so that one wrong line cannot hide in the whole-matrix error;
   * on every matrix of a refresh step, Lemma 1's band: for a non-square [A, B]
     matrix whose normalised singular values are all >= 2e-3 (true for these
     Gaussian / Student-t inputs), RMS(O) * sqrt(max(A, B)) lies in [0.68, 1.21].
@@ -24,7 +27,7 @@ import pytest
 from oracle import muon_oracle as O
 from matrix_orthogonalising_optimizer_02_amd import binding as B
 from matrix_orthogonalising_optimizer_02_amd import workloads as WL
-from tolerances import FP32_TOL, NS_TOL
+from tolerances import FP32_TOL, assert_ns_close
 
 pytestmark = pytest.mark.gpu
 
@@ -123,9 +126,32 @@ def test_fullsize_refresh_step(torch_dev, wl):
         s = wl.shapes[i]
         g64 = host(g[i])
         ref = -HP.lr * HP.rms_scale * math.sqrt(max(s)) * O.newton_schulz(g64)
-        err = rel_fro(host(w[i]), ref)
-        log(f"  matrix {i} {s}: update rel err {err:.3e}")
-        assert err < NS_TOL, (s, err)
+        err, line = assert_ns_close(host(w[i]), ref, s, i)
+        log(f"  matrix {i} {s}: update rel err {err:.3e}, worst line {line:.3e}")
+
+
+@pytest.mark.timeout(900)
+def test_fullsize_refresh_15b_largest_matrices(torch_dev):
+    """The 15B-scale set's refresh step with W = 0, all ten matrices in one call; its
+    largest tall matrix [30720, 5120] (the longest Gram, K = 30720) and its flat
+    [5120, 20480] matrix against the oracle's NS5 (about 50 TFLOP of float64 work on
+    the host, one matrix at a time)."""
+    torch, dev = torch_dev
+    wl = WL.LAYER_SET_15B_H5120
+    w, m, g = fill_state(torch, dev, wl, w_zero=True)
+    ws = B.make_workspace(wl.shapes, dev)
+    log(f"refresh step, {wl.name}, W = 0")
+    B.muon_step(w, m, g, 0, B.default_hparams(period_k=3), ws)
+    torch.cuda.synchronize()
+    del ws, m
+    for want in ((30720, 5120), (5120, 20480)):
+        i = wl.shapes.index(want)
+        g64 = host(g[i])
+        log(f"  matrix {i} {want}: oracle NS5 on the host")
+        ref = -HP.lr * HP.rms_scale * math.sqrt(max(want)) * O.newton_schulz(g64)
+        err, line = assert_ns_close(host(w[i]), ref, want, i)
+        log(f"  matrix {i} {want}: update rel err {err:.3e}, worst line {line:.3e}")
+        del g64, ref
 
 
 @pytest.mark.parametrize("wl", FULL, ids=lambda w: f"key{w.key}")
@@ -151,8 +177,9 @@ def test_fullsize_periodic_schedule_mixed_bucket(torch_dev):
     """The 16-matrix [2048,8192]/[8192,2048] bucket over 12 steps with K = 3 at full size.
 
     Every step: M' elementwise on sampled lines. RowNorm steps: W' on sampled lines.
-    Refresh steps: the Lemma 1 band on every matrix, and at step 0 the oracle's NS5 on
-    one flat and one tall matrix.
+    Refresh steps: the Lemma 1 band on every matrix, and at steps 0 and 9 the oracle's
+    NS5 on one flat and one tall matrix, from the state the GPU's earlier steps left
+    (teacher forced: the oracle advances that state by one step).
     """
     torch, dev = torch_dev
     wl = WL.MIXED_BUCKET_H2048
@@ -172,7 +199,7 @@ def test_fullsize_periodic_schedule_mixed_bucket(torch_dev):
         before = [(take_lines(w[i], s, lines[i]), take_lines(m[i], s, lines[i]), take_lines(g[i], s, lines[i]))
                   for i, s in enumerate(wl.shapes)]
         full = None
-        if step == 0:
+        if step in (0, 9):
             full = {i: (host(w[i]), host(m[i]), host(g[i])) for i in (0, 1)}
         w_prev = [x.clone() for x in w] if refresh else None
         log(f"step {step} ({'refresh' if refresh else 'rownorm'})")
@@ -193,9 +220,8 @@ def test_fullsize_periodic_schedule_mixed_bucket(torch_dev):
                 s = wl.shapes[i]
                 o = O.newton_schulz(HP.mu * m0 + g0)
                 upd_ref = -HP.lr * HP.rms_scale * math.sqrt(max(s)) * o
-                err = rel_fro(host(w[i]) - decay * w0, upd_ref)
-                log(f"  matrix {i} {s}: update rel err {err:.3e}")
-                assert err < NS_TOL
+                err, line = assert_ns_close(host(w[i]) - decay * w0, upd_ref, s, (step, i))
+                log(f"  matrix {i} {s}: update rel err {err:.3e}, worst line {line:.3e}")
 
 
 @pytest.mark.parametrize("wl", [WL.MIXED_BUCKET_H2048, WL.LAYER_SET_15B_H5120], ids=lambda w: f"key{w.key}")
@@ -217,9 +243,8 @@ def test_fullsize_eq6_refresh_and_monitor(torch_dev, wl):
     i = min(range(len(wl.shapes)), key=lambda k: wl.shapes[k][0] * wl.shapes[k][1])
     o = O.newton_schulz(host(g[i]))
     ref = -HP.lr * 0.2 * o / math.sqrt(float(np.mean(o * o)))
-    err = rel_fro(host(w[i]), ref)
-    log(f"  matrix {i} {wl.shapes[i]}: update rel err {err:.3e}")
-    assert err < NS_TOL
+    err, line = assert_ns_close(host(w[i]), ref, wl.shapes[i], i)
+    log(f"  matrix {i} {wl.shapes[i]}: update rel err {err:.3e}, worst line {line:.3e}")
 
 
 def test_fullsize_monitor_periodic_cycle_15b(torch_dev):

@@ -5,7 +5,8 @@ Each case draws a set of 1-12 matrices with independent random shapes (each side
 residue modulo the 4-, 64- and 256-element blockings, a random step index and period K (so refresh and RowNorm steps both
 occur), a random update-scale rule, and the monitor on or off. Refresh steps are
 checked through the W = 0 probe (the update itself) at the bf16 Newton-Schulz
-tolerance (2e-2, 4e-2 when min(A, B) < 64, derived in tolerances.py); RowNorm steps
+tolerance (2e-2, wider bands when min(A, B) < 64, from tolerances.py) and its per-line
+bound; RowNorm steps
 and the momentum at the
 fp32 tolerance 1e-5; the monitor against the oracle at the same tolerances.
 """
@@ -17,7 +18,7 @@ import pytest
 from oracle import muon_oracle as O
 from matrix_orthogonalising_optimizer_02_amd import binding as B
 from matrix_orthogonalising_optimizer_02_amd import workloads as WL
-from tolerances import FP32_TOL, ns_tol
+from tolerances import FP32_TOL, assert_ns_close, ns_tol
 
 pytestmark = pytest.mark.gpu
 
@@ -81,7 +82,10 @@ def test_random_sets_vs_oracle(torch_dev, seed, max_side, max_count):
         if ew > worst:
             worst, worst_shape = ew, s
         assert em < FP32_TOL, (seed, s, "momentum", em)
-        assert ew < tol, (seed, s, "update", ew, tol)
+        if refresh:  # W = 0 probe: W' is the update, held per line as well
+            assert_ns_close(w[i].cpu().numpy(), w_ref, s, (seed, "update"))
+        else:
+            assert ew < tol, (seed, s, "update", ew, tol)
         if monitor:
             assert abs(rms_h[i] - u_rms) <= tol * abs(u_rms) + 1e-12, (seed, s, "monitor", rms_h[i], u_rms)
     log(f"seed {seed}: worst update error {worst:.2e} at {worst_shape}")
