@@ -5,6 +5,7 @@ library next to this file; the Python binding loads it from there.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -47,14 +48,18 @@ def build(verbose: bool = False, defines=(), out: str = LIB_PATH) -> str:
     dflags = [f"-D{d}" for d in defines]
     tmp = tempfile.mkdtemp(prefix="muon_build_")
     try:
-        objs = []
+        cmds, objs = [], []
         for src in SOURCES:
             path = os.path.join(CSRC, src)
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmd = [cc, *COMMON_FLAGS, *dflags, *lang, "-c", path, "-o", obj]
-            _run(cmd, verbose)
+            cmds.append([cc, *COMMON_FLAGS, *dflags, *lang, "-c", path, "-o", obj])
             objs.append(obj)
+        # the sources compile independently; at most `jobs` compilers at once
+        jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "0") or 0) or os.cpu_count() or 1, 8))
+        with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+            for f in [pool.submit(_run, c, verbose) for c in cmds]:
+                f.result()
         out_tmp = out + ".tmp"
         _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", out_tmp], verbose)
         os.replace(out_tmp, out)
