@@ -194,6 +194,29 @@ int ns5_batched(const float* const* m_in, float* const* o_out, const int64_t* ro
 int rownorm_update(const muon_matrix* mats, int32_t count, const muon_hparams* hp,
                    void* workspace, size_t workspace_bytes, float* update_rms, void* stream);
 
+/* ---- Allocation-free RowNorm step ---------------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. The same step as rownorm_update() (the
+ * same kernels in the same order: bitwise identical results), with its workspace taken
+ * from a fixed array of MUON_NOALLOC_SCRATCH_BYTES in device memory that the library
+ * holds: one copy on each GPU it runs on, kept until the process ends. The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine) and creates
+ * no timing events.
+ * Limit: the RowNorm workspace of the matrices must fit the array. Per group of up to
+ * 16 matrices (the same grouping as muon_step) it is the sum over the group of
+ *   tall [A, B] (A > B):  4 B (ceil(A / 256) + 2) bytes,
+ *   flat [A, B]:          4 A bytes,
+ * each part rounded up to 256 bytes; sixteen [30720, 5120] matrices take 40 MB. Beyond
+ * it the call returns MUON_ERR_WORKSPACE and nothing runs.
+ * Every call on one GPU uses that GPU's single array: calls that overlap in time on one
+ * GPU (other streams, other threads) race and corrupt each other's results; serialise
+ * them. The array keeps the last call's contents; no part of it needs to start at zero.
+ * Errors: as rownorm_update (WORKSPACE for the limit), HIP when the current device or the
+ * array's address cannot be looked up. */
+#define MUON_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int rownorm_update_noalloc(const muon_matrix* mats, int32_t count, const muon_hparams* hp,
+                           float* update_rms, void* stream);
+
 /* ---- One GPU's share of a row-sharded RowNorm step --------------------------------
  * "Scaling Muon for Diffusion Transformers", distributed-implementation paragraph: with
  * the weights sharded by rows (dim 0) across GPUs, the rows of a flat matrix (A <= B)

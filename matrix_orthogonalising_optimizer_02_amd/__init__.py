@@ -25,6 +25,7 @@ from .binding import (  # noqa: F401
     rownorm_shard_colsq,
     rownorm_shard_workspace_bytes,
     rownorm_update,
+    rownorm_update_noalloc,
     svd_entropy,
     svd_entropy_workspace_bytes,
     timing_enable,

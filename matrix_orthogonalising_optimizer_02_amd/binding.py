@@ -32,6 +32,7 @@ KCLASS_NAMES = ("cast", "frob", "gram", "poly", "apply", "apply_final", "rownorm
 
 EXPORTED = ("muon_abi_version", "muon_status_str", "muon_last_error", "muon_default_hparams",
             "muon_workspace_bytes", "ns5_plan", "muon_step", "ns5_batched", "rownorm_update",
+            "rownorm_update_noalloc",
             "adamw_default_hparams", "adamw_step", "svd_entropy_workspace_bytes", "svd_entropy",
             "rownorm_shard_workspace_bytes", "rownorm_shard_colsq", "rownorm_shard_apply",
             "muon_timing_enable", "muon_timing_read")
@@ -103,6 +104,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ns5_batched.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_int64),
                                 ctypes.POINTER(ctypes.c_int64), i32, ctypes.POINTER(MuonHParams), vp, sz, vp]
     lib.rownorm_update.argtypes = [ctypes.POINTER(MuonMatrix), i32, ctypes.POINTER(MuonHParams), vp, sz, vp, vp]
+    lib.rownorm_update_noalloc.argtypes = [ctypes.POINTER(MuonMatrix), i32, ctypes.POINTER(MuonHParams), vp, vp]
     lib.adamw_default_hparams.argtypes = [ctypes.POINTER(AdamWHParams)]
     lib.adamw_default_hparams.restype = None
     lib.adamw_step.argtypes = [ctypes.POINTER(AdamWParam), i32, ctypes.POINTER(AdamWHParams), i64, vp]
@@ -117,8 +119,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                         ctypes.POINTER(vp), vp, sz, vp]
     lib.muon_timing_enable.argtypes = [ctypes.c_int]
     lib.muon_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
-    for name in ("muon_step", "ns5_batched", "rownorm_update", "muon_workspace_bytes", "ns5_plan", "adamw_step",
-                 "svd_entropy_workspace_bytes", "svd_entropy", "rownorm_shard_workspace_bytes",
+    for name in ("muon_step", "ns5_batched", "rownorm_update", "rownorm_update_noalloc", "muon_workspace_bytes",
+                 "ns5_plan", "adamw_step", "svd_entropy_workspace_bytes", "svd_entropy", "rownorm_shard_workspace_bytes",
                  "rownorm_shard_colsq", "rownorm_shard_apply", "muon_timing_enable", "muon_timing_read"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
@@ -297,6 +299,18 @@ def rownorm_update(weights, momenta, grads, hp: Optional[MuonHParams] = None, wo
     rc = load_library().rownorm_update(arr, len(weights), ctypes.byref(hp), ws, wsb,
                                        _monitor_ptr(update_rms, len(weights)), _stream_handle(stream, dev))
     _check(rc, "rownorm_update")
+
+
+def rownorm_update_noalloc(weights, momenta, grads, hp: Optional[MuonHParams] = None, stream=None,
+                           update_rms=None):
+    """rownorm_update on the library's fixed device scratch: allocates nothing (for graph
+    capture and serving loops). Calls that overlap in time on one GPU race."""
+    hp = hp or default_hparams()
+    arr = _matrices(weights, momenta, grads)
+    dev = weights[0].device if weights else None
+    rc = load_library().rownorm_update_noalloc(arr, len(weights), ctypes.byref(hp),
+                                               _monitor_ptr(update_rms, len(weights)), _stream_handle(stream, dev))
+    _check(rc, "rownorm_update_noalloc")
 
 
 def ns5_batched(inputs, outputs=None, hp: Optional[MuonHParams] = None, workspace=None, stream=None):

@@ -18,7 +18,7 @@ LIB_NAME = "libmuon_rocm.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["k_elementwise.hip", "k_gemm.hip", "k_adamw.hip", "k_spectrum.hip", "muon_abi.cpp"]
+SOURCES = ["k_elementwise.hip", "k_gemm.hip", "k_adamw.hip", "k_spectrum.hip", "noalloc.hip", "muon_abi.cpp"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -27,6 +27,7 @@
 #include <vector>
 
 #include "../../include/muon_rocm.h"
+#include "abi_internal.hpp"
 #include "launch.hpp"
 
 #define MUON_API extern "C" __attribute__((visibility("default")))
@@ -68,6 +69,7 @@ struct MatPlan {
 struct GroupPlan {
     std::vector<MatPlan> mats;
     size_t bytes = 0;
+    size_t rn_bytes = 0;      // the part the RowNorm step uses (column partials, norms, monitor)
     size_t tail = 0;          // fp32 partial tiles of the stages that split their tail
     int64_t tail_units = 0;
 };
@@ -189,6 +191,7 @@ GemmTile choose_tile(const GroupPlan& gp, bool sym, int stage) {
 struct Plan {
     std::vector<GroupPlan> groups;
     size_t bytes = 0;
+    size_t rn_bytes = 0;      // the largest group's RowNorm part
 };
 
 int make_plan(const int64_t* rows, const int64_t* cols, int32_t count, Plan* plan) {
@@ -221,6 +224,7 @@ int make_plan(const int64_t* rows, const int64_t* cols, int32_t count, Plan* pla
     });
     plan->groups.clear();
     plan->bytes = 0;
+    plan->rn_bytes = 0;
     for (size_t s = 0; s < all.size(); s += kMaxGroup) {
         GroupPlan gp;
         size_t ns = 0, rn = 0;
@@ -270,7 +274,9 @@ int make_plan(const int64_t* rows, const int64_t* cols, int32_t count, Plan* pla
             }
         }
         gp.bytes = std::max(ns, rn);
+        gp.rn_bytes = rn;
         plan->bytes = std::max(plan->bytes, gp.bytes);
+        plan->rn_bytes = std::max(plan->rn_bytes, rn);
         plan->groups.push_back(std::move(gp));
     }
     return MUON_OK;
@@ -289,6 +295,10 @@ struct Timing {
     std::vector<hipEvent_t> pool;
 } g_timing;
 
+// Nonzero while a call that must not create events (the allocation-free entry point)
+// enqueues its kernels: the timing facility then leaves them unbracketed.
+thread_local int g_untimed = 0;
+
 hipEvent_t take_event() {
     if (!g_timing.pool.empty()) {
         hipEvent_t e = g_timing.pool.back();
@@ -306,7 +316,7 @@ int run_kernel(int cls, hipStream_t s, const char* name, F&& launch) {
     bool timed = false;
     {
         std::lock_guard<std::mutex> lk(g_timing.mu);
-        if (g_timing.enabled) {
+        if (g_timing.enabled && !g_untimed) {
             a = take_event();
             b = take_event();
             timed = a && b;
@@ -948,6 +958,52 @@ int run_spectrum(const std::vector<SpMat>& g, const float* const* w, char* ws, d
 }
 
 }  // namespace
+
+// The RowNorm step on a scratch buffer the library holds (the allocation-free entry
+// point, csrc/noalloc.hip). Every argument is validated and the step planned on the
+// host first; only then, and only when there is work, does get_scratch fetch the
+// current device's scratch address. Groups run one after another on the same region,
+// as with a caller's workspace; every scratch element a kernel reads was written
+// earlier in the same call, so nothing has to start at zero. No event is created
+// for the timing facility.
+int rownorm_noalloc_impl(const muon_matrix* mats, int32_t count, const muon_hparams* hp, float* update_rms,
+                         void* stream, size_t scratch_cap, void* (*get_scratch)(std::string* error)) {
+    g_last_error.clear();
+    int rc = check_hparams(hp, false);
+    if (rc) return rc;
+    std::vector<int64_t> rows, cols;
+    std::vector<Range> ranges;
+    rc = check_matrices(mats, count, rows, cols, ranges);
+    if (rc) return rc;
+    rc = check_monitor(update_rms, count, ranges);
+    if (rc) return rc;
+    Plan plan;
+    rc = make_plan(rows.data(), cols.data(), count, &plan);
+    if (rc) return rc;
+    if (plan.rn_bytes > scratch_cap)
+        return fail(MUON_ERR_WORKSPACE, "these matrices need " + std::to_string(plan.rn_bytes) +
+                                            " bytes of scratch; the library's fixed scratch holds " +
+                                            std::to_string(scratch_cap) + " (call rownorm_update with a workspace)");
+    rc = check_overlaps(ranges);
+    if (rc) return rc;
+    if (plan.groups.empty()) return MUON_OK;
+    std::string err;
+    char* ws = static_cast<char*>(get_scratch(&err));
+    if (!ws) return fail(MUON_ERR_HIP, "scratch address: " + err);
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(ws);
+    ranges.push_back({lo, lo + plan.rn_bytes, true});
+    rc = check_overlaps(ranges);  // a caller's buffer inside the library's scratch
+    if (rc) return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    ++g_untimed;
+    for (const GroupPlan& gp : plan.groups) {
+        rc = run_rownorm(gp, mats, *hp, ws, update_rms, s);
+        if (rc) break;
+    }
+    --g_untimed;
+    return rc;
+}
+
 }  // namespace muon
 
 using namespace muon;

@@ -397,3 +397,23 @@ def test_shard_calls_validation(lib):
     assert colsq(shard_arr([(64, 32, 100), (50, 32, 100)]), 2, s=overlap) == B.MUON_ERR_ALIAS
     assert lib.rownorm_shard_apply(shard_arr([(64, 32, 100)]), 1, ctypes.byref(hp), None,
                                    ctypes.c_void_p(BASE * 4), 1 << 34, None) == B.MUON_ERR_INVALID_ARG
+
+
+@fake_only
+def test_noalloc_validation_and_size_limit(lib):
+    hp = B.default_hparams()
+    rn = lib.rownorm_update_noalloc
+    assert rn(None, 0, ctypes.byref(hp), None, None) == B.MUON_OK
+    assert rn(mats([(16, 32)]), 1, None, None, None) == B.MUON_ERR_INVALID_ARG
+    assert rn(mats([(16, 32)], align=4), 1, ctypes.byref(hp), None, None) == B.MUON_ERR_ALIGN
+    assert rn(mats([(16, 32)], w_off=0, m_off=0), 1, ctypes.byref(hp), None, None) == B.MUON_ERR_ALIAS
+    # one tall [262144, 16384] matrix needs 4 * 16384 * (1024 + 2) bytes, above the 64 MiB scratch
+    big = (B.MuonMatrix * 1)(B.MuonMatrix(262144, 16384, BASE, BASE * 2, BASE * 3))
+    assert rn(big, 1, ctypes.byref(hp), None, None) == B.MUON_ERR_WORKSPACE
+    assert b"scratch" in lib.muon_last_error()
+    # sixteen [30720, 5120] tall matrices (about 40 MB) fit; with no GPU the device lookup fails
+    arr = (B.MuonMatrix * 16)()
+    for i in range(16):
+        span = 1 << 30
+        arr[i] = B.MuonMatrix(30720, 5120, BASE + span * (3 * i), BASE + span * (3 * i + 1), BASE + span * (3 * i + 2))
+    assert rn(arr, 16, ctypes.byref(hp), None, None) == B.MUON_ERR_HIP
