@@ -14,8 +14,9 @@ of one whole cycle. Also reported: the vanilla (every step NS5) step time, NS5
 TFLOP/s, RowNorm GB/s, the dominant kernel against its roofline (per-launch
 HIP-event durations recorded by the library on the launch stream), the same step
 figures for the other multi-matrix workloads (the H = 2048 DiT block, the 16-matrix
-bucket, the H = 3072 MMDiT pair), and the float64 oracle timed on a bounded sample on
-the host cores.
+bucket, the H = 3072 MMDiT pair), the attainable ceilings measured in the same run
+(the library's streaming copy kernel and its register-only MFMA loop, beside the spec
+peaks), and the float64 oracle timed on a bounded sample on the host cores.
 """
 from __future__ import annotations
 
@@ -167,6 +168,8 @@ def parse():
                     help="eager vs HIP-graph-replayed Periodic cycles on the small workloads (0 = skip)")
     ap.add_argument("--config-cycles", type=int, default=10,
                     help="timed Periodic cycles (and vanilla steps) on each other multi-matrix workload (0 = skip)")
+    ap.add_argument("--ceiling-reps", type=int, default=5,
+                    help="calls per window of the copy and MFMA-loop ceilings (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-traffic", nargs=5, metavar=("CAL_FETCH", "CAL_WRITE", "RUN_FETCH", "RUN_WRITE", "OUT"),
                     help="write the HBM traffic record from rocprofv3 counter CSVs and exit (no GPU)")
@@ -565,6 +568,49 @@ def measure_shard_rownorm(pkg, torch, dev, wl, degree, reps, rn_ms, say):
     return res
 
 
+def measure_ceilings(pkg, torch, dev, reps, say):
+    """The attainable ceilings on this GPU in this run, beside the spec peaks: the
+    library's streaming copy kernel over 1 GiB (read + write bytes per second) and its
+    register-only bf16 MFMA loop on one block per compute unit. Medians of five event
+    windows."""
+    def median_ms(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(n):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) / n)
+        return sorted(out)[2]
+
+    n = 1 << 28  # 1 GiB of fp32
+    src = torch.empty(n, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    copy_ms = median_ms(lambda: pkg.ceiling_copy(src, dst), 4 * reps)
+    assert torch.equal(src[:4096], dst[:4096]) and torch.equal(src[-4096:], dst[-4096:])
+    copy_gbs = 8.0 * n / (copy_ms * 1e-3) / 1e9
+    del src, dst
+    blocks, iters = 256, 100000
+    chk = torch.zeros(4 * blocks, dtype=torch.float32, device=dev)
+    flops = pkg.ceiling_mfma(chk, blocks, iters)
+    mfma_ms = median_ms(lambda: pkg.ceiling_mfma(chk, blocks, iters), max(1, reps // 2))
+    assert bool(torch.isfinite(chk).all())
+    mfma_tflops = flops / (mfma_ms * 1e-3) / 1e12
+    res = {"copy": {"gbs": round(copy_gbs, 1), "frac_of_spec": round(copy_gbs / PEAK_HBM_GBS, 4),
+                    "bytes_per_call": 8 * n, "ms_per_call": round(copy_ms, 4),
+                    "kernel": "muon_ceiling_copy: 256 threads, 16 KiB per block, non-temporal"},
+           "mfma": {"tflops": round(mfma_tflops, 1), "frac_of_spec": round(mfma_tflops / PEAK_BF16_TFLOPS, 4),
+                    "flops_per_call": flops, "ms_per_call": round(mfma_ms, 4),
+                    "kernel": "muon_ceiling_mfma: 256 blocks x 4 waves, 16 independent 32x32x16 bf16 MFMA chains "
+                              "per wave, operand bits toggling every round as a GEMM's do, no memory traffic"}}
+    say(f"ceilings: {res}")
+    return res
+
+
 def measure_graph(pkg, torch, dev, n, say):
     """Eager Periodic cycles against the same cycle captured once in a HIP graph and
     replayed, on the small workloads where launches dominate (the 128 x 512 matrix and
@@ -716,6 +762,7 @@ def main():
     shard = measure_shard_rownorm(pkg, torch, dev, wl, args.shard_degree, 50, rn_ms, say) \
         if args.shard_degree > 1 else None
     graph = measure_graph(pkg, torch, dev, args.graph_cycles, say) if args.graph_cycles > 0 else None
+    ceilings = measure_ceilings(pkg, torch, dev, args.ceiling_reps, say) if args.ceiling_reps > 0 else None
     others = [w for w in ("dit2048", "bucket2048", "mmdit3072", "15b") if w != args.workload]
     configs = measure_configs(pkg, torch, dev, others, args.config_cycles, say) if args.config_cycles > 0 else None
     # dominant kernel: the B X product of iterations 1..N-1
@@ -801,6 +848,11 @@ def main():
         out["graph_replay"] = graph
     if configs is not None:
         out["configs"] = configs
+    if ceilings is not None:
+        ceilings["apply_frac_of_mfma_ceiling"] = round(apply_tflops / ceilings["mfma"]["tflops"], 4)
+        ceilings["ns5_frac_of_mfma_ceiling"] = round(ns5_tflops / ceilings["mfma"]["tflops"], 4)
+        ceilings["rownorm_frac_of_copy_ceiling"] = round(rn_gbs / ceilings["copy"]["gbs"], 4)
+        out["ceilings"] = ceilings
     if not args.no_cpu_baseline:
         say("cpu baseline: timing the float64 oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(wl, k)

@@ -333,6 +333,24 @@ int svd_entropy(const float* const* w, const int64_t* rows, const int64_t* cols,
                 void* workspace, size_t workspace_bytes, double* entropy, double* sigma_sq,
                 void* stream);
 
+/* ---- Attainable ceilings ------------------------------------------------------------
+ * Yardsticks for the two rooflines the step is measured against, timed by the caller
+ * (HIP events on `stream`) on the same GPU; neither is part of the optimizer step.
+ * muon_ceiling_copy: dst[i] = src[i] for n fp32 elements (DEVICE pointers, 16-byte
+ *   aligned, not overlapping), streamed as the step's HBM-bound passes stream: 256
+ *   threads, 16 KiB contiguous per block, all loads of a thread before its stores,
+ *   non-temporal hints. 8 n bytes of HBM traffic. Errors: INVALID_ARG, ALIGN, ALIAS,
+ *   TOO_LARGE, HIP.
+ * muon_ceiling_mfma: `blocks` blocks of four waves; every wave issues `iters` rounds of
+ *   16 independent v_mfma_f32_32x32x16_bf16 on register operands into 16 fp32 32 x 32
+ *   accumulators (the register budget of a Newton-Schulz GEMM wave), then writes one
+ *   checksum to out[4 block + wave] (DEVICE, 4 blocks floats, 4-byte aligned). *flops
+ *   (host, may be NULL) receives the dense flop count, blocks * 4 * iters * 16 * 32768.
+ *   One block per compute unit (256 blocks) keeps one wave on every SIMD, as the GEMMs
+ *   do. Errors: INVALID_ARG, ALIGN, HIP. */
+int muon_ceiling_copy(const float* src, float* dst, int64_t n, void* stream);
+int muon_ceiling_mfma(float* out, int32_t blocks, int32_t iters, double* flops, void* stream);
+
 /* Optional per-kernel-class timing. While enabled (enable != 0), every kernel the
  * library enqueues is bracketed by HIP events recorded on the caller's stream (a GEMM
  * stage that splits its last tiles over K is bracketed together with its fixup

@@ -15,6 +15,8 @@ from .binding import (  # noqa: F401
     MuonOptimizer,
     adamw_default_hparams,
     adamw_step,
+    ceiling_copy,
+    ceiling_mfma,
     default_hparams,
     load_library,
     make_workspace,

@@ -18,7 +18,8 @@ LIB_NAME = "libmuon_rocm.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["k_elementwise.hip", "k_gemm.hip", "k_adamw.hip", "k_spectrum.hip", "noalloc.hip", "muon_abi.cpp"]
+SOURCES = ["k_elementwise.hip", "k_gemm.hip", "k_adamw.hip", "k_spectrum.hip", "noalloc.hip", "k_ceiling.hip",
+           "muon_abi.cpp"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
@@ -38,14 +39,27 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libmuon_rocm.so")
 
 
-def build(verbose: bool = False, defines=(), out: str = LIB_PATH) -> str:
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer (the device code is built
+# as usual: -Xarch_host keeps every sanitizer option on the host compilation).
+SANITIZE_HOST_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-g",
+]
+SANITIZED_LIB_PATH = os.path.join(PKG_DIR, "libmuon_rocm_hostsan.so")
+
+
+def build(verbose: bool = False, defines=(), out: str = LIB_PATH, host_sanitize: bool = False) -> str:
     """Compile all sources and link the shared library; returns its path.
 
     `defines` are extra -D options (tile-configuration constants); `out` places the
-    library elsewhere, e.g. to compare configurations side by side.
+    library elsewhere, e.g. to compare configurations side by side. host_sanitize
+    builds the host code with AddressSanitizer and UndefinedBehaviorSanitizer, for
+    CPU-only runs of the C ABI's validation paths; load it with the sanitizer runtime
+    preloaded (sanitizer_runtime()).
     """
     cc = hipcc()
-    dflags = [f"-D{d}" for d in defines]
+    dflags = [f"-D{d}" for d in defines] + (SANITIZE_HOST_FLAGS if host_sanitize else [])
     tmp = tempfile.mkdtemp(prefix="muon_build_")
     try:
         cmds, objs = [], []
@@ -61,11 +75,23 @@ def build(verbose: bool = False, defines=(), out: str = LIB_PATH) -> str:
             for f in [pool.submit(_run, c, verbose) for c in cmds]:
                 f.result()
         out_tmp = out + ".tmp"
-        _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", out_tmp], verbose)
+        link_san = ["-shared-libsan", *SANITIZE_HOST_FLAGS[:4]] if host_sanitize else []
+        _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *link_san, *objs, "-o", out_tmp], verbose)
         os.replace(out_tmp, out)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
     return out
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (it carries the
+    UndefinedBehaviorSanitizer handlers too), to preload for the sanitized library."""
+    res = subprocess.run([os.path.join(os.path.dirname(hipcc()), "..", "llvm", "bin", "clang"),
+                          "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.exists(path):
+        raise RuntimeError("the compiler's AddressSanitizer runtime was not found")
+    return os.path.realpath(path)
 
 
 def _run(cmd, verbose):

@@ -10,6 +10,9 @@
 
 namespace muon {
 
+// Sets this thread's muon_last_error() text and returns `code`; an empty text clears it.
+int set_last_error(int code, const std::string& what);
+
 // rownorm_update on a scratch buffer of scratch_cap bytes that get_scratch returns for
 // the current device (NULL with *error set on failure). Validates and plans on the host
 // before get_scratch is called; rejects matrices whose RowNorm workspace exceeds

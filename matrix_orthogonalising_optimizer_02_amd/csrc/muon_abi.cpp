@@ -959,6 +959,8 @@ int run_spectrum(const std::vector<SpMat>& g, const float* const* w, char* ws, d
 
 }  // namespace
 
+int set_last_error(int code, const std::string& what) { return fail(code, what); }
+
 // The RowNorm step on a scratch buffer the library holds (the allocation-free entry
 // point, csrc/noalloc.hip). Every argument is validated and the step planned on the
 // host first; only then, and only when there is work, does get_scratch fetch the

@@ -417,3 +417,18 @@ def test_noalloc_validation_and_size_limit(lib):
         span = 1 << 30
         arr[i] = B.MuonMatrix(30720, 5120, BASE + span * (3 * i), BASE + span * (3 * i + 1), BASE + span * (3 * i + 2))
     assert rn(arr, 16, ctypes.byref(hp), None, None) == B.MUON_ERR_HIP
+
+
+@fake_only
+def test_ceiling_argument_errors(lib):
+    cp, mf = lib.muon_ceiling_copy, lib.muon_ceiling_mfma
+    assert cp(None, None, 0, None) == B.MUON_OK
+    assert cp(None, ctypes.c_void_p(BASE), 16, None) == B.MUON_ERR_INVALID_ARG
+    assert cp(ctypes.c_void_p(BASE), ctypes.c_void_p(BASE * 2), -1, None) == B.MUON_ERR_INVALID_ARG
+    assert cp(ctypes.c_void_p(BASE + 4), ctypes.c_void_p(BASE * 2), 16, None) == B.MUON_ERR_ALIGN
+    assert cp(ctypes.c_void_p(BASE), ctypes.c_void_p(BASE + 32), 16, None) == B.MUON_ERR_ALIAS
+    flops = ctypes.c_double(-1.0)
+    assert mf(None, 0, 10, ctypes.byref(flops), None) == B.MUON_OK and flops.value == 0.0
+    assert mf(None, 4, 10, None, None) == B.MUON_ERR_INVALID_ARG
+    assert mf(ctypes.c_void_p(BASE), -1, 10, None, None) == B.MUON_ERR_INVALID_ARG
+    assert mf(ctypes.c_void_p(BASE + 2), 4, 10, None, None) == B.MUON_ERR_ALIGN
