@@ -95,8 +95,8 @@ typedef struct muon_matrix {
 #define MUON_KCLASS_CAST 0          /* momentum + Frobenius partials + bf16 working copies */
 #define MUON_KCLASS_FROB 1          /* per-matrix 1 / max(||M||_F, eps) */
 #define MUON_KCLASS_GRAM 2          /* A = X X^T (symmetric tiles, bf16 MFMA; with its tail fixup) */
-#define MUON_KCLASS_POLY 3          /* B = b A + c A A (symmetric tiles, bf16 MFMA; with its tail fixup) */
-#define MUON_KCLASS_APPLY 4         /* X' = a X + B X, iterations 1..N-1 (with its tail fixup) */
+#define MUON_KCLASS_POLY 3          /* P = a I + b A + c A A (symmetric tiles, bf16 MFMA; with its tail fixup) */
+#define MUON_KCLASS_APPLY 4         /* X' = P X = a X + (b A + c A A) X, iterations 1..N-1 (with its tail fixup) */
 #define MUON_KCLASS_APPLY_FINAL 5   /* last iteration: O out, or the fused Eq. 4 update */
 #define MUON_KCLASS_ROWNORM_ROWS 6  /* one-pass RowNorm step, flat / square matrices */
 #define MUON_KCLASS_COLNORM_PARTIAL 7  /* tall: momentum + per-column partial sums */
@@ -132,8 +132,9 @@ void muon_default_hparams(muon_hparams* hp);
 int muon_workspace_bytes(const int64_t* rows, const int64_t* cols, int32_t count, size_t* bytes);
 
 /* The GEMM plan of the Newton-Schulz stages (Eq. 2 of the Muon scaling paper: the Gram
- * X X^T, the polynomial b A + c A A, the Apply a X + B X) that ns5_batched and the
- * refresh step of muon_step use for `count` matrices of shapes rows[i] x cols[i].
+ * X X^T, the polynomial P = a I + b A + c A A, the Apply P X = a X + (b A + c A A) X)
+ * that ns5_batched and the refresh step of muon_step use for `count` matrices of
+ * shapes rows[i] x cols[i].
  * Host only, touches no device; for tests and capacity planning. Nonempty matrices are
  * grouped as those calls group them: sorted by m = min(rows, cols), then by
  * n = max(rows, cols), both descending (stable), at most 16 per group. *groups receives

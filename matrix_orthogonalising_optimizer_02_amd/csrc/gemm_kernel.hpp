@@ -3,9 +3,14 @@
 //
 // Each iteration is three products, all of the form C[i][j] = sum_k P[i][k] Q[j][k]
 // with both operands K-contiguous in HBM:
-//   Gram  A = X X^T   P = Q = X_r ([m_p, n_p])       K = n_p   symmetric output
-//   Poly  B = bA+cAA  P = Q = A   ([m_p, m_p])       K = m_p   symmetric (A = A^T)
-//   Apply X' = aX+BX  P = B, Q = X_c ([n_p, m_p])    K = m_p   X'_r and X'_c out
+//   Gram  A = X X^T            P = Q = X_r ([m_p, n_p])      K = n_p   symmetric output
+//   Poly  P = aI + bA + cAA    P = Q = A   ([m_p, m_p])      K = m_p   symmetric (A = A^T)
+//   Apply X' = P X             P = P, Q = X_c ([n_p, m_p])   K = m_p   X'_r and X'_c out
+// X' = a X + (b A + c A^2) X is computed as (a I + b A + c A^2) X: the polynomial's
+// epilogue adds a to the diagonal before its bf16 rounding, so the Apply is a plain
+// product whose epilogue reads no operand. (Measured with a CPU emulation of the bf16
+// rounding against the float64 iteration: this is also the more accurate recipe, since
+// the diagonal a + B_ii that gets rounded is smaller than B_ii.)
 // Symmetric outputs compute only upper-triangular tiles and store each tile twice
 // (mirrored). The first iteration folds s = 1 / ||M||_F into the Gram (s^2) and
 // Apply (s) epilogues. The last Apply writes fp32 O in the input's orientation, or
@@ -563,6 +568,7 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
     // flat / tall matrix). Operands of the epilogue math (X for a X, the mirrored half
     // of A for b A) are read where a lane's 4 rows are contiguous.
     constexpr int HN = Cfg::HN, NBH = TN / 2;     // columns and 32-column blocks per half
+    constexpr int kWN = WM * HN / 4 / 64;          // fused update: W float4 per lane and half
     constexpr int TSB = WM + 8, DSB = HN + 8;     // bf16 strides: transposed, direct
     constexpr int TSF = WM + 4, DSF = HN + 4;     // fp32 strides
     const float first_s = args.first ? *d.scale : 1.0f;
@@ -591,21 +597,18 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
     const float g2 = first_s * first_s;
     float sq = 0.f;  // final modes: this lane's sum of O^2 (padding contributes exact zeros)
 
-    // Operand of the epilogue math of the polynomial and Apply stages (the mirrored half
-    // of A for b A, X for a X), per half: HN rows j of WM values i, 256 bytes each,
-    // brought in through LDS so that every global access is a full 256-byte row segment
-    // (16 lanes per row, 4 rows per 1 KiB DMA load) instead of 32 rows x 8 bytes per
-    // instruction. Chunk c of row r is stored at position c ^ (r & 15). The block sits
-    // over the direct-staging area: it is read into registers before any staging write,
-    // and x_dma waits until earlier LDS reads of the area are done. The Apply with the
-    // fused update takes this path for its first half only: for the second, the wait
-    // for the block would also wait for the first half's W stores, so it keeps direct
-    // loads (measured: 16 x [2048, 8192] last Apply 1.58-1.64 -> 1.55 ms, spills 30 -> 2).
-    constexpr bool kDmaX = (MODE == kModePoly || MODE == kModeApply || MODE == kModeFinalW) && Cfg::kDirect &&
-                           WM == 128 && HN == 64;
+    // Operand of the polynomial's epilogue math (the mirrored half of A for b A), per
+    // half: HN rows j of WM values i, 256 bytes each, brought in through LDS so that every
+    // global access is a full 256-byte row segment (16 lanes per row, 4 rows per 1 KiB DMA
+    // load) instead of 32 rows x 8 bytes per instruction. Chunk c of row r is stored at
+    // position c ^ (r & 15). The block sits over the direct-staging area: it is read into
+    // registers before any staging write, and x_dma waits until earlier LDS reads of the
+    // area are done. The Apply stages read no operand here: the polynomial stage has
+    // folded a I into P, so their epilogue only scales the product.
+    constexpr bool kDmaX = MODE == kModePoly && Cfg::kDirect && WM == 128 && HN == 64;
     unsigned short* const xs = sA + __builtin_amdgcn_readfirstlane(wave) * (Cfg::kEpiWave / 2) + HN * TSB;
     auto x_dma = [&](int hh) {
-        const unsigned short* src = (MODE == kModePoly) ? d.a : d.xc;
+        const unsigned short* src = d.a;
         const int64_t lds = d.m_p;
         wait_lgkm0();
         const int lr = lane >> 4, lp = lane & 15;
@@ -631,16 +634,55 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        // operands of the epilogue math for this half: 8 contiguous bytes per (a, b, rg)
+        // Each half's loads stay inside the half: hoisting the second half's W loads above
+        // the first half's stores would hold both halves of W in registers and spill.
+        __builtin_amdgcn_sched_barrier(0);
+        const int colh0 = col_base + h * HN;  // first global column of this half
+        // Fused update: this half's W is loaded first, so that its latency overlaps the
+        // staging of O below. A tall W is [n, m] (row j holds WM consecutive i of the
+        // tile), a flat one [m, n] (row i holds HN consecutive j of the half); both are
+        // kWN float4 per lane.
+        floatx4 wv[kWN];
+        if constexpr (MODE == kModeFinalW) {
+            if (d.tall) {
+                constexpr int CH = WM / 4;
+#pragma unroll
+                for (int it = 0; it < kWN; ++it) {
+                    const int c = it * 64 + lane, r = c / CH, k = c % CH;
+                    const int j = colh0 + r, i = row_base + k * 4;
+                    if (j < d.n && ((d.m & 3) == 0) && i + 3 < d.m)
+                        wv[it] = *reinterpret_cast<const floatx4*>(d.out + (int64_t)j * d.m + i);
+                    else
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            wv[it][e] = (j < d.n && i + e < d.m) ? d.out[(int64_t)j * d.m + i + e] : 0.f;
+                }
+            } else {
+                constexpr int CH = HN / 4;
+#pragma unroll
+                for (int it = 0; it < kWN; ++it) {
+                    const int c = it * 64 + lane, r = c / CH, k = c % CH;
+                    const int i = row_base + r, j = colh0 + k * 4;
+                    if (i < d.m && ((d.n & 3) == 0) && j + 3 < d.n)
+                        wv[it] = *reinterpret_cast<const floatx4*>(d.out + (int64_t)i * d.n + j);
+                    else
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            wv[it][e] = (i < d.m && j + e < d.n) ? d.out[(int64_t)i * d.n + j + e] : 0.f;
+                }
+            }
+        }
+        // operands of the polynomial's epilogue math for this half: 8 contiguous bytes
+        // per (a, b, rg)
         u32x2 opv[TM][NBH][4];
-        if constexpr (MODE != kModeGram) {
-            if (kDmaX && (MODE != kModeFinalW || h == 0)) {
+        if constexpr (MODE == kModePoly) {
+            if (kDmaX) {
                 x_dma(h);
                 wait_vmcnt<0>();
                 x_read(opv);
             } else {
-                const unsigned short* src = (MODE == kModePoly) ? d.a : d.xc;
-                const int64_t lds = d.m_p;  // A is [m_p, m_p]; X_c is [n_p, m_p]
+                const unsigned short* src = d.a;
+                const int64_t lds = d.m_p;  // A is [m_p, m_p]
 #pragma unroll
                 for (int a = 0; a < TM; ++a)
 #pragma unroll
@@ -667,12 +709,16 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
                         float x = acc[a][b][rg * 4 + e];
                         if constexpr (MODE == kModeGram) {
                             x *= g2;
-                        } else {
+                        } else if constexpr (MODE == kModePoly) {
                             const u32x2 w = opv[a][bb][rg];
                             const unsigned w32 = (e < 2) ? w.x : w.y;
                             const float o = bf2f((unsigned short)((e & 1) ? (w32 >> 16) : (w32 & 0xffff)));
-                            if constexpr (MODE == kModePoly) x = fmaf(args.cb, o, args.cc * x);
-                            else x = fmaf(args.ca, o, x) * first_s;
+                            x = fmaf(args.cb, o, args.cc * x);
+                            // P = a I + b A + c A A: a on the diagonal of the real rows
+                            const int gi = row_base + il + e;
+                            if (ti == tj && gi == colh0 + jl && gi < d.m) x += args.ca;
+                        } else {
+                            x *= first_s;  // P X, and s on the first iteration
                         }
                         v[e] = x;
                         if constexpr (!kBf16Out) sq = fmaf(x, x, sq);
@@ -701,7 +747,7 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
             }
         }
         wait_lgkm0();  // this wave's staging writes are complete before its lanes read them
-        const int colh = col_base + h * HN;  // first global column of this half
+        const int colh = colh0;
         if constexpr (kBf16Out) {
             // transposed rows: HN rows of WM values (WM / 8 chunks each)
             if (dst_t) {
@@ -728,22 +774,10 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         } else if (d.tall) {
             // O / W is [n, m]: row j holds WM consecutive i of this tile (WM / 4 chunks)
             constexpr int CH = WM / 4, N = HN * CH / 64;
-            floatx4 wv[N];
-            if constexpr (MODE == kModeFinalW) {
-#pragma unroll
-                for (int it = 0; it < N; ++it) {
-                    const int c = it * 64 + lane, r = c / CH, k = c % CH;
-                    const int j = colh + r, i = row_base + k * 4;
-                    if (j < d.n && ((d.m & 3) == 0) && i + 3 < d.m)
-                        wv[it] = *reinterpret_cast<const floatx4*>(d.out + (int64_t)j * d.m + i);
-                    else
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            wv[it][e] = (j < d.n && i + e < d.m) ? d.out[(int64_t)j * d.m + i + e] : 0.f;
-                }
-            }
+            static_assert(N == kWN, "W staging");
 #pragma unroll
             for (int it = 0; it < N; ++it) {
+                if (it % 8 == 0) __builtin_amdgcn_sched_barrier(0);  // at most 8 LDS reads ahead
                 const int c = it * 64 + lane, r = c / CH, k = c % CH;
                 const int j = colh + r, i = row_base + k * 4;
                 floatx4 o = *reinterpret_cast<const floatx4*>(lf + r * TSF + k * 4);
@@ -762,22 +796,10 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         } else {
             // O / W is [m, n]: row i holds HN consecutive j of this half (HN / 4 chunks)
             constexpr int CH = HN / 4, N = WM * CH / 64;
-            floatx4 wv[N];
-            if constexpr (MODE == kModeFinalW) {
-#pragma unroll
-                for (int it = 0; it < N; ++it) {
-                    const int c = it * 64 + lane, r = c / CH, k = c % CH;
-                    const int i = row_base + r, j = colh + k * 4;
-                    if (i < d.m && ((d.n & 3) == 0) && j + 3 < d.n)
-                        wv[it] = *reinterpret_cast<const floatx4*>(d.out + (int64_t)i * d.n + j);
-                    else
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            wv[it][e] = (i < d.m && j + e < d.n) ? d.out[(int64_t)i * d.n + j + e] : 0.f;
-                }
-            }
+            static_assert(N == kWN, "W staging");
 #pragma unroll
             for (int it = 0; it < N; ++it) {
+                if (it % 8 == 0) __builtin_amdgcn_sched_barrier(0);  // at most 8 LDS reads ahead
                 const int c = it * 64 + lane, r = c / CH, k = c % CH;
                 const int i = row_base + r, j = colh + k * 4;
                 floatx4 o = *reinterpret_cast<const floatx4*>(lf + r * DSF + k * 4);

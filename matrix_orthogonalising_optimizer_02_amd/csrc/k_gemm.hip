@@ -40,9 +40,9 @@ __global__ __launch_bounds__(256, (Cfg::kLdsBytes > 80 * 1024) ? 1 : 2) void k_n
 // index of one tail tile, adds the tile's chunks in chunk order and applies the stage's
 // epilogue arithmetic, as the tile epilogue does:
 //   Gram        A = s2 acc, bf16 at (i, j) and, off the diagonal, at (j, i);
-//   polynomial  B = b A + c acc (A read at (j, i)), stored the same way;
-//   Apply       X' = s1 (a X + acc) (X read from X_c at (j, i)), bf16 into X'_c at
-//               (j, i) and into the row-major X'_r at (i, j) when the next Gram reads it.
+//   polynomial  P = a [i == j < m] + b A + c acc (A read at (j, i)), stored the same way;
+//   Apply       X' = s1 acc, bf16 into X'_c at (j, i) and into the row-major X'_r at
+//               (i, j) when the next Gram reads it.
 // kTailUnitFloats / 1024 blocks per tail tile.
 template <int MODE>
 __global__ __launch_bounds__(256) void k_ns_tail_fix(NsArgs args) {
@@ -81,14 +81,18 @@ __global__ __launch_bounds__(256) void k_ns_tail_fix(NsArgs args) {
         const int j = tj * 256 + (wave & 1) * 128 + b * 32 + ((lane0 + q) & 31);
         float y = v[q];
         if constexpr (MODE == kModeApply) {
-            y = fmaf(args.ca, bf2f(d.xc[kb_off(j, i, ld)]), y) * s1;
+            y *= s1;
             const unsigned short h = f2bf(y);
             d.xc_next[kb_off(j, i, ld)] = h;
             if (d.xr_next) d.xr_next[(int64_t)i * d.n_p + j] = h;
         } else {
             unsigned short* dst = (MODE == kModeGram) ? d.a : d.b;
-            if constexpr (MODE == kModeGram) y *= g2;
-            else y = fmaf(args.cb, bf2f(d.a[kb_off(j, i, ld)]), args.cc * y);
+            if constexpr (MODE == kModeGram) {
+                y *= g2;
+            } else {
+                y = fmaf(args.cb, bf2f(d.a[kb_off(j, i, ld)]), args.cc * y);
+                if (i == j && i < d.m) y += args.ca;  // P = a I + b A + c A A
+            }
             const unsigned short h = f2bf(y);
             dst[kb_off(i, j, ld)] = h;
             if (ti != tj) dst[kb_off(j, i, ld)] = h;

@@ -51,9 +51,9 @@ struct FrobArgs {
 // to [m_p, n_p]. X_r is X row-major [m_p, n_p]; X_c is X^T row-major [n_p, m_p].
 enum GemmMode : int {
     kModeGram = 0,     // A = s2 * X X^T                  (symmetric tiles)
-    kModePoly = 1,     // B = b A + c A A                  (symmetric tiles)
-    kModeApply = 2,    // X' = s1 * (a X + B X)            bf16 X'_c, and X'_r if xr_next
-    kModeFinalO = 3,   // O  = s1 * (a X + B X)            fp32, input orientation
+    kModePoly = 1,     // P = a I + b A + c A A            (symmetric tiles; a on real rows only)
+    kModeApply = 2,    // X' = s1 * P X                    bf16 X'_c, and X'_r if xr_next
+    kModeFinalO = 3,   // O  = s1 * P X                    fp32, input orientation
     kModeFinalW = 4,   // W <- decay W - upd_coef O        fused Eq. 4 update
 };
 
