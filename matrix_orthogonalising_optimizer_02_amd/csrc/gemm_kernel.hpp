@@ -562,13 +562,19 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
 
     // ---- epilogue. Accumulator element r of a 32x32 block sits at row
     // 8*(r/4) + 4*(lane/32) + r%4, column lane%32: each lane owns 4 consecutive rows of
-    // one column. Results are staged per wave through LDS, half of the wave's columns at
+    // one column. Results are staged per wave through LDS, a chunk of the wave's columns at
     // a time, and leave in 16-byte row chunks: the direct orientation C[i][j] and/or the
     // transposed one C[j][i] (X'_r / X'_c, a symmetric tile and its mirror, or W of a
-    // flat / tall matrix). Operands of the epilogue math (X for a X, the mirrored half
+    // flat / tall matrix). Operands of the epilogue math (the mirrored half
     // of A for b A) are read where a lane's 4 rows are contiguous.
-    constexpr int HN = Cfg::HN, NBH = TN / 2;     // columns and 32-column blocks per half
-    constexpr int kWN = WM * HN / 4 / 64;          // fused update: W float4 per lane and half
+    // The wave's columns leave in NCH chunks of HN: halves, or quarters for the fused
+    // update, whose W loads for the next quarter are issued while the current one is
+    // staged and stored (two quarters of W fit the registers, two halves do not).
+    constexpr int NCH = (MODE == kModeFinalW && TN >= 4) ? 4 : 2;
+    constexpr int HN = WN / NCH, NBH = TN / NCH;   // columns and 32-column blocks per chunk
+    static_assert(NBH >= 1 && NBH * NCH == TN, "whole 32-column blocks per chunk");
+    static_assert(HN <= Cfg::HN, "a chunk fits the staging area");
+    constexpr int kWN = WM * HN / 4 / 64;          // fused update: W float4 per lane and chunk
     constexpr int TSB = WM + 8, DSB = HN + 8;     // bf16 strides: transposed, direct
     constexpr int TSF = WM + 4, DSF = HN + 4;     // fp32 strides
     const float first_s = args.first ? *d.scale : 1.0f;
@@ -632,47 +638,52 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
                 }
     };
 
+    // Fused update: W of chunk h as kWN float4 per lane. A tall W is [n, m] (row j holds
+    // WM consecutive i of the tile), a flat one [m, n] (row i holds HN consecutive j of
+    // the chunk).
+    floatx4 wbuf[2][kWN];
+    auto load_w = [&](floatx4 (&wv)[kWN], int hh) {
+        const int colh0 = col_base + hh * HN;
+        if (d.tall) {
+            constexpr int CH = WM / 4;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        // Each half's loads stay inside the half: hoisting the second half's W loads above
-        // the first half's stores would hold both halves of W in registers and spill.
-        __builtin_amdgcn_sched_barrier(0);
-        const int colh0 = col_base + h * HN;  // first global column of this half
-        // Fused update: this half's W is loaded first, so that its latency overlaps the
-        // staging of O below. A tall W is [n, m] (row j holds WM consecutive i of the
-        // tile), a flat one [m, n] (row i holds HN consecutive j of the half); both are
-        // kWN float4 per lane.
-        floatx4 wv[kWN];
-        if constexpr (MODE == kModeFinalW) {
-            if (d.tall) {
-                constexpr int CH = WM / 4;
+            for (int it = 0; it < kWN; ++it) {
+                const int c = it * 64 + lane, r = c / CH, k = c % CH;
+                const int j = colh0 + r, i = row_base + k * 4;
+                if (j < d.n && ((d.m & 3) == 0) && i + 3 < d.m)
+                    wv[it] = *reinterpret_cast<const floatx4*>(d.out + (int64_t)j * d.m + i);
+                else
 #pragma unroll
-                for (int it = 0; it < kWN; ++it) {
-                    const int c = it * 64 + lane, r = c / CH, k = c % CH;
-                    const int j = colh0 + r, i = row_base + k * 4;
-                    if (j < d.n && ((d.m & 3) == 0) && i + 3 < d.m)
-                        wv[it] = *reinterpret_cast<const floatx4*>(d.out + (int64_t)j * d.m + i);
-                    else
+                    for (int e = 0; e < 4; ++e)
+                        wv[it][e] = (j < d.n && i + e < d.m) ? d.out[(int64_t)j * d.m + i + e] : 0.f;
+            }
+        } else {
+            constexpr int CH = HN / 4;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            wv[it][e] = (j < d.n && i + e < d.m) ? d.out[(int64_t)j * d.m + i + e] : 0.f;
-                }
-            } else {
-                constexpr int CH = HN / 4;
+            for (int it = 0; it < kWN; ++it) {
+                const int c = it * 64 + lane, r = c / CH, k = c % CH;
+                const int i = row_base + r, j = colh0 + k * 4;
+                if (i < d.m && ((d.n & 3) == 0) && j + 3 < d.n)
+                    wv[it] = *reinterpret_cast<const floatx4*>(d.out + (int64_t)i * d.n + j);
+                else
 #pragma unroll
-                for (int it = 0; it < kWN; ++it) {
-                    const int c = it * 64 + lane, r = c / CH, k = c % CH;
-                    const int i = row_base + r, j = colh0 + k * 4;
-                    if (i < d.m && ((d.n & 3) == 0) && j + 3 < d.n)
-                        wv[it] = *reinterpret_cast<const floatx4*>(d.out + (int64_t)i * d.n + j);
-                    else
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            wv[it][e] = (i < d.m && j + e < d.n) ? d.out[(int64_t)i * d.n + j + e] : 0.f;
-                }
+                    for (int e = 0; e < 4; ++e)
+                        wv[it][e] = (i < d.m && j + e < d.n) ? d.out[(int64_t)i * d.n + j + e] : 0.f;
             }
         }
-        // operands of the polynomial's epilogue math for this half: 8 contiguous bytes
+    };
+    if constexpr (MODE == kModeFinalW) load_w(wbuf[0], 0);
+
+#pragma unroll
+    for (int h = 0; h < NCH; ++h) {
+        // A chunk's work stays inside the chunk, apart from the next chunk's W loads,
+        // which are issued here so that they overlap this chunk's staging and stores.
+        __builtin_amdgcn_sched_barrier(0);
+        const int colh0 = col_base + h * HN;  // first global column of this chunk
+        if constexpr (MODE == kModeFinalW) {
+            if (h + 1 < NCH) load_w(wbuf[(h + 1) & 1], h + 1);
+        }
+        // operands of the polynomial's epilogue math for this chunk: 8 contiguous bytes
         // per (a, b, rg)
         u32x2 opv[TM][NBH][4];
         if constexpr (MODE == kModePoly) {
@@ -699,7 +710,7 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
 #pragma unroll
             for (int bb = 0; bb < NBH; ++bb) {
                 const int b = h * NBH + bb;
-                const int jl = bb * 32 + lj;  // column within the half
+                const int jl = bb * 32 + lj;  // column within the chunk
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
                     const int il = a * 32 + rg * 8 + li;  // first of 4 rows within the wave tile
@@ -783,7 +794,7 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
                 floatx4 o = *reinterpret_cast<const floatx4*>(lf + r * TSF + k * 4);
                 if constexpr (MODE == kModeFinalW) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = fmaf(-d.upd_coef, o[e], wv[it][e] * args.decay);
+                    for (int e = 0; e < 4; ++e) o[e] = fmaf(-d.upd_coef, o[e], wbuf[h & 1][it][e] * args.decay);
                 }
                 if (j < d.n && ((d.m & 3) == 0) && i + 3 < d.m) {
                     *reinterpret_cast<floatx4*>(d.out + (int64_t)j * d.m + i) = o;
@@ -794,7 +805,7 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
                 }
             }
         } else {
-            // O / W is [m, n]: row i holds HN consecutive j of this half (HN / 4 chunks)
+            // O / W is [m, n]: row i holds HN consecutive j of this chunk (HN / 4 float4)
             constexpr int CH = HN / 4, N = WM * CH / 64;
             static_assert(N == kWN, "W staging");
 #pragma unroll
@@ -805,7 +816,7 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
                 floatx4 o = *reinterpret_cast<const floatx4*>(lf + r * DSF + k * 4);
                 if constexpr (MODE == kModeFinalW) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = fmaf(-d.upd_coef, o[e], wv[it][e] * args.decay);
+                    for (int e = 0; e < 4; ++e) o[e] = fmaf(-d.upd_coef, o[e], wbuf[h & 1][it][e] * args.decay);
                 }
                 if (i < d.m && ((d.n & 3) == 0) && j + 3 < d.n) {
                     *reinterpret_cast<floatx4*>(d.out + (int64_t)i * d.n + j) = o;
@@ -816,7 +827,7 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
                 }
             }
         }
-        // the next half overwrites the staging area: LDS executes a wave's operations in
+        // the next chunk overwrites the staging area: LDS executes a wave's operations in
         // order, so its writes cannot overtake the reads above
     }
     if constexpr (!kBf16Out) {
