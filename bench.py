@@ -828,7 +828,7 @@ def main():
             "periodic_over_vanilla": round((cycle_ms / k) / vanilla_ms, 4),
             "pages_periodic_over_vanilla_15b": round(1.317 / 2.884, 4),
             "note": "one MI355X, optimizer step only, no communication"}),
-        "roofline": {"bound": "mfma", "kernel": "k_ns_gemm<apply> (B X, iterations 1..4; with its tail fixup where split)",
+        "roofline": {"bound": "mfma", "kernel": "k_ns_gemm<apply> (P X, iterations 1..4; with its tail fixup where split)",
                      "achieved": round(apply_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(apply_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(["k_ns_gemm<2, muon::GemmCfg<256, 256, true, 32, 4>, true>",
