@@ -571,8 +571,8 @@ def measure_shard_rownorm(pkg, torch, dev, wl, degree, reps, rn_ms, say):
 def measure_ceilings(pkg, torch, dev, reps, say):
     """The attainable ceilings on this GPU in this run, beside the spec peaks: the
     library's streaming copy kernel over 1 GiB (read + write bytes per second) and its
-    register-only bf16 MFMA loop on one block per compute unit. Medians of five event
-    windows."""
+    register-only bf16 MFMA loop on one block per compute unit; and torch's bf16 GEMM as
+    a yardstick. Medians of five event windows."""
     def median_ms(fn, n):
         fn()
         torch.cuda.synchronize()
@@ -607,6 +607,19 @@ def measure_ceilings(pkg, torch, dev, reps, say):
                     "flops_per_call": flops, "ms_per_call": round(mfma_ms, 4),
                     "kernel": "muon_ceiling_mfma: 256 blocks x 4 waves, 16 independent 32x32x16 bf16 MFMA chains "
                               "per wave, operand bits toggling every round as a GEMM's do, no memory traffic"}}
+    # the vendor GEMM as a yardstick (torch.matmul, hipBLASLt on this image): bf16
+    # operands, fp32 accumulation, bf16 out; 8192^3, and the Apply's largest product
+    # (P [5120, 5120] times X [5120, 30720])
+    yard = {}
+    for name, (mm, kk, nn) in (("8192^3", (8192, 8192, 8192)), ("apply_5120x5120x30720", (5120, 5120, 30720))):
+        a = torch.randn(mm, kk, device=dev).to(torch.bfloat16)
+        bm = torch.randn(kk, nn, device=dev).to(torch.bfloat16)
+        c = torch.empty(mm, nn, device=dev, dtype=torch.bfloat16)
+        ms = median_ms(lambda: torch.matmul(a, bm, out=c), max(2, reps))
+        tf = 2.0 * mm * kk * nn / (ms * 1e-3) / 1e12
+        yard[name] = {"tflops": round(tf, 1), "frac_of_spec": round(tf / PEAK_BF16_TFLOPS, 4), "ms_per_call": round(ms, 4)}
+        del a, bm, c
+    res["torch_matmul_bf16"] = yard
     say(f"ceilings: {res}")
     return res
 
@@ -852,6 +865,8 @@ def main():
         ceilings["apply_frac_of_mfma_ceiling"] = round(apply_tflops / ceilings["mfma"]["tflops"], 4)
         ceilings["ns5_frac_of_mfma_ceiling"] = round(ns5_tflops / ceilings["mfma"]["tflops"], 4)
         ceilings["rownorm_frac_of_copy_ceiling"] = round(rn_gbs / ceilings["copy"]["gbs"], 4)
+        yard = ceilings["torch_matmul_bf16"]["apply_5120x5120x30720"]["tflops"]
+        ceilings["apply_vs_torch_matmul_same_shape"] = round(apply_tflops / yard, 4)
         out["ceilings"] = ceilings
     if not args.no_cpu_baseline:
         say("cpu baseline: timing the float64 oracle on a sample")
