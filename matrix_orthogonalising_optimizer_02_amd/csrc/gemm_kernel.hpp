@@ -310,43 +310,43 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         // the wave index is uniform: keep it scalar so the LDS destinations (M0) are too
         const int swave = __builtin_amdgcn_readfirstlane(wave);
         const int lrow = lane / CPR, lpc = lane % CPR;
-        int64_t offa[Cfg::IA], offb[Cfg::IB];
-#pragma unroll
-        for (int q = 0; q < Cfg::IA; ++q) {
-            if constexpr (kTr) {  // slot s: rows (s & 3) + 8 (s >> 2) and that + 4
-                const int sl = swave * Cfg::IA + q;
-                const int row = (sl & 3) + 8 * (sl >> 2) + 4 * (lane >> 5);
-                const int c = lane & 31;  // 16-byte chunk of the row's 256 columns
-                offa[q] = ((int64_t)(c >> 2) << 13) + row * 32 + ((c & 3) << 3);
-            } else {  // K-contiguous rows of the tile's panel, K step = one 32-column block
-                const int row = (swave * Cfg::IA + q) * RPI + lrow;
-                offa[q] = (int64_t)row * BK + ((lpc ^ ((row >> Cfg::SWS) & (CPR - 1))) << 3);
-            }
+        // The loads are buffer loads to LDS: a resource over the tile's panel (scalar
+        // registers), a per-lane byte offset that is the same for every load and K step
+        // (vector), and a block-uniform byte offset per load and K step (scalar). No load
+        // needs vector address arithmetic.
+        // Load q of this wave covers slot (or 16-row group) swave * I + q:
+        //   K-major tiles: lane l fetches 16-byte chunk (l & 31) of row 4 (l >> 5) of the
+        //   slot's row pair, rows (s & 3) + 8 (s >> 2) (+ 4) of the K step's 32;
+        //   K-contiguous tiles: lane l fetches row l / CPR of the group at the swizzled
+        //   chunk position, and the swizzle depends on the lane alone (the group's first
+        //   row is a multiple of RPI, which keeps (row >> SWS) mod CPR to the lane's part).
+        static_assert(kTr || ((RPI >> Cfg::SWS) % CPR) == 0, "swizzle independent of the load index");
+        uint32_t lane_off;  // bytes
+        if constexpr (kTr) {
+            const int c = lane & 31;
+            lane_off = 2u * (((uint32_t)(c >> 2) << 13) + 4 * (lane >> 5) * 32 + ((c & 3) << 3));
+        } else {
+            lane_off = 2u * (uint32_t)(lrow * BK + ((lpc ^ ((lrow >> Cfg::SWS) & (CPR - 1))) << 3));
         }
-#pragma unroll
-        for (int q = 0; q < Cfg::IB; ++q) {
-            if constexpr (kTr) {
-                const int sl = swave * Cfg::IB + q;
-                const int row = (sl & 3) + 8 * (sl >> 2) + 4 * (lane >> 5);
-                const int c = lane & 31;
-                offb[q] = ((int64_t)(c >> 2) << 13) + row * 32 + ((c & 3) << 3);
-            } else {
-                const int row = (swave * Cfg::IB + q) * RPI + lrow;
-                offb[q] = (int64_t)row * BK + ((lpc ^ ((row >> Cfg::SWS) & (CPR - 1))) << 3);
-            }
-        }
+        auto slot_off = [&](int sl) -> uint32_t {  // bytes, block-uniform
+            if constexpr (kTr) return 2u * (uint32_t)(((sl & 3) + 8 * (sl >> 2)) * 32);
+            else return 2u * (uint32_t)(sl * RPI * BK);
+        };
+        const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)Pt, (short)0, 0x7FFFFFFF, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)Qt, (short)0, 0x7FFFFFFF, 0x00020000);
         // one 1 KiB load (idx < LOADS) into the stage whose A and B tiles start at dA, dB
         auto gload = [&](unsigned short* dA, unsigned short* dB, int k0, int idx) {
             // K-major: rows k0 .. k0 + 31 of panel k0 / 256; otherwise block k0 / 32
-            const int64_t kofs = kTr ? ((((int64_t)(k0 >> 8) * (ld >> 5)) << 13) + ((k0 & 255) << 5))
-                                     : ((int64_t)(k0 >> 5) << 13);
+            const uint32_t kofs = 2u * (uint32_t)(kTr ? ((((int64_t)(k0 >> 8) * (ld >> 5)) << 13) + ((k0 & 255) << 5))
+                                                      : ((int64_t)(k0 >> 5) << 13));
             constexpr int SLOT = kTr ? Cfg::kTrSlot : 512;
             if (idx < Cfg::IA)
-                __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Pt + offa[idx] + kofs),
-                                                 (lds_ptr_t)(dA + (swave * Cfg::IA + idx) * SLOT), 16, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(dA + (swave * Cfg::IA + idx) * SLOT), 16,
+                                                         lane_off, kofs + slot_off(swave * Cfg::IA + idx), 0, 0);
             else
-                __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Qt + offb[idx - Cfg::IA] + kofs),
-                                                 (lds_ptr_t)(dB + (swave * Cfg::IB + idx - Cfg::IA) * SLOT), 16, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(dB + (swave * Cfg::IB + idx - Cfg::IA) * SLOT),
+                                                         16, lane_off, kofs + slot_off(swave * Cfg::IB + idx - Cfg::IA), 0,
+                                                         0);
         };
         // Fragments are double-buffered in registers (K-major tiles: as two halves).
         bf16x8 fa[2][TM], fb[2][TN];
