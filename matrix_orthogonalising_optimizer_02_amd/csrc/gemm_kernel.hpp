@@ -115,6 +115,11 @@ struct BoolC {
 };
 
 template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
+
+template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
@@ -236,7 +241,7 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         xcd_slot(args, x, sl, gi, local);
     }
     if (gi < 0) return;
-    const NsDesc& d = args.d[gi];
+    const NsDesc d = args.d[gi];  // a copy: the kernel arguments are then read only at fixed or indexed offsets
 
     int ti, tj;
     if constexpr (kSym) tri_tile(local, d.tiles, ti, tj);
@@ -332,8 +337,16 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
             if constexpr (kTr) return 2u * (uint32_t)(((sl & 3) + 8 * (sl >> 2)) * 32);
             else return 2u * (uint32_t)(sl * RPI * BK);
         };
-        const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)Pt, (short)0, 0x7FFFFFFF, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)Qt, (short)0, 0x7FFFFFFF, 0x00020000);
+        // the panel bases are block-uniform; reading them through readfirstlane tells the
+        // compiler so (a resource it takes for per-lane data costs a loop per load)
+        auto uniform_ptr = [](const unsigned short* q) -> void* {
+            const uint64_t v = reinterpret_cast<uint64_t>(q);
+            const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+            const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+            return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+        };
+        const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(Pt), (short)0, 0x7FFFFFFF, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(Qt), (short)0, 0x7FFFFFFF, 0x00020000);
         // one 1 KiB load (idx < LOADS) into the stage whose A and B tiles start at dA, dB
         auto gload = [&](unsigned short* dA, unsigned short* dB, int k0, int idx) {
             // K-major: rows k0 .. k0 + 31 of panel k0 / 256; otherwise block k0 / 32
@@ -419,11 +432,16 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         // gets a wait for every outstanding load; the explicit waits above already order
         // each read after the loads of its own stage.
         static_assert(STAGES >= 3, "the load stage must differ from the stages read");
-        auto kstep = [&](int kt, auto more_c, auto next_c) {
+        // phase_c: IntC<p> when kt % STAGES == p is known at compile time (the stage
+        // offsets then fold into the LDS instructions' immediate offsets), IntC<-1> when not.
+        auto kstep = [&](int kt, auto more_c, auto next_c, auto phase_c) {
             constexpr bool MORE = decltype(more_c)::value;
             constexpr bool NEXT = decltype(next_c)::value;
-            const int lbuf = (kt + STAGES - 1) % STAGES, lk0 = (kt + STAGES - 1) * BK;
-            const int cur = kt % STAGES, nxt = (kt + 1) % STAGES;
+            constexpr int PH = decltype(phase_c)::value;
+            const int lk0 = (kt + STAGES - 1) * BK;
+            const int lbuf = PH >= 0 ? (PH + STAGES - 1) % STAGES : (kt + STAGES - 1) % STAGES;
+            const int cur = PH >= 0 ? PH : kt % STAGES;
+            const int nxt = PH >= 0 ? (PH + 1) % STAGES : (kt + 1) % STAGES;
             const int last_issued = min(kt + STAGES - 1, nk - 1);
             auto body = [&](unsigned short* __restrict__ dA, unsigned short* __restrict__ dB,
                             const unsigned short* __restrict__ cA, const unsigned short* __restrict__ cB,
@@ -434,7 +452,9 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
                     const bool last = kk == KK - 1;
                     if (last && NEXT) {
                         wait_lgkm0();
-                        wait_step(kt + 1, last_issued);
+                        // a step that issues loads has issued STAGES - 2 steps beyond kt + 1
+                        if constexpr (MORE) wait_vmcnt<LOADS * (STAGES - 2)>();
+                        else wait_step(kt + 1, last_issued);
                         barrier_no_fence();
                     }
                     __builtin_amdgcn_sched_barrier(0);
@@ -456,10 +476,20 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
             body(sA + lbuf * STAGE_A, sB + lbuf * STAGE_B, sA + cur * STAGE_A, sB + cur * STAGE_B,
                  sA + nxt * STAGE_A, sB + nxt * STAGE_B);
         };
+        // The steps that issue loads run unrolled by the ring depth, so that every stage
+        // offset is a constant; the few steps after them (at most STAGES - 1 that still
+        // issue loads, then the STAGES - 1 that drain the ring) compute their stages.
+        static_assert(STAGES == 4, "the unrolled K loop has four phases");
         int kt = 0;
-        for (; kt + STAGES - 1 < nk; ++kt) kstep(kt, BoolC<true>{}, BoolC<true>{});
-        for (; kt + 1 < nk; ++kt) kstep(kt, BoolC<false>{}, BoolC<true>{});
-        if (kt < nk) kstep(kt, BoolC<false>{}, BoolC<false>{});
+        for (; kt + STAGES - 1 + 3 < nk; kt += 4) {
+            kstep(kt, BoolC<true>{}, BoolC<true>{}, IntC<0>{});
+            kstep(kt + 1, BoolC<true>{}, BoolC<true>{}, IntC<1>{});
+            kstep(kt + 2, BoolC<true>{}, BoolC<true>{}, IntC<2>{});
+            kstep(kt + 3, BoolC<true>{}, BoolC<true>{}, IntC<3>{});
+        }
+        for (; kt + STAGES - 1 < nk; ++kt) kstep(kt, BoolC<true>{}, BoolC<true>{}, IntC<-1>{});
+        for (; kt + 1 < nk; ++kt) kstep(kt, BoolC<false>{}, BoolC<true>{}, IntC<-1>{});
+        if (kt < nk) kstep(kt, BoolC<false>{}, BoolC<false>{}, IntC<-1>{});
         __syncthreads();
         if constexpr (kSplit) {
             if (chunk >= 0) {  // a tail chunk: partial sums out, the fixup finishes the tile
