@@ -272,13 +272,17 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         Qt = Q + (int64_t)tj * BN * ld;
     }
 
+    // The direct-load path starts the accumulators with its first K step's MFMAs (a zero
+    // accumulator input) instead of writing 16 zeros into each of them.
     floatx16 acc[TM][TN];
+    if constexpr (!Cfg::kDirect) {
 #pragma unroll
-    for (int a = 0; a < TM; ++a)
+        for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < TN; ++b)
+            for (int b = 0; b < TN; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+                for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+    }
 
     // K steps of this block: all of K, or chunk c of nsplit, cut at multiples of 256 (K
     // is one): the chunk's start is then a fixed offset of the tile's operand pointers
@@ -434,10 +438,11 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         static_assert(STAGES >= 3, "the load stage must differ from the stages read");
         // phase_c: IntC<p> when kt % STAGES == p is known at compile time (the stage
         // offsets then fold into the LDS instructions' immediate offsets), IntC<-1> when not.
-        auto kstep = [&](int kt, auto more_c, auto next_c, auto phase_c) {
+        auto kstep = [&](int kt, auto more_c, auto next_c, auto phase_c, auto first_c) {
             constexpr bool MORE = decltype(more_c)::value;
             constexpr bool NEXT = decltype(next_c)::value;
             constexpr int PH = decltype(phase_c)::value;
+            constexpr bool FIRST = decltype(first_c)::value;  // K step 0: accumulators start at zero
             const int lk0 = (kt + STAGES - 1) * BK;
             const int lbuf = PH >= 0 ? (PH + STAGES - 1) % STAGES : (kt + STAGES - 1) % STAGES;
             const int cur = PH >= 0 ? PH : kt % STAGES;
@@ -461,8 +466,19 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
 #pragma unroll
                     for (int i = 0; i < NMF; ++i) {
                         const int a = i / TN, b = i % TN;
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa(fbuf, a), opb(fbuf, b), acc[a][b],
-                                                                           0, 0, 0);
+                        if constexpr (FIRST) {
+                            if (kk == 0) {
+                                const floatx16 zero = {};
+                                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa(fbuf, a), opb(fbuf, b), zero,
+                                                                                   0, 0, 0);
+                            } else {
+                                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa(fbuf, a), opb(fbuf, b),
+                                                                                   acc[a][b], 0, 0, 0);
+                            }
+                        } else {
+                            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opa(fbuf, a), opb(fbuf, b), acc[a][b],
+                                                                               0, 0, 0);
+                        }
                         if (i < NFR) {
                             if (!last) frag(fbuf ^ 1, cA, cB, kk + 1, i);
                             else if (NEXT) frag(fbuf ^ 1, nA, nB, 0, i);
@@ -479,17 +495,22 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         // The steps that issue loads run unrolled by the ring depth, so that every stage
         // offset is a constant; the few steps after them (at most STAGES - 1 that still
         // issue loads, then the STAGES - 1 that drain the ring) compute their stages.
+        // K step 0 (which issues loads: K is at least one 256-wide unit, 8 steps) runs
+        // first, on its own, with zero accumulator inputs.
         static_assert(STAGES == 4, "the unrolled K loop has four phases");
-        int kt = 0;
+        constexpr BoolC<true> T{};
+        constexpr BoolC<false> F{};
+        kstep(0, T, T, IntC<0>{}, T);
+        int kt = 1;
         for (; kt + STAGES - 1 + 3 < nk; kt += 4) {
-            kstep(kt, BoolC<true>{}, BoolC<true>{}, IntC<0>{});
-            kstep(kt + 1, BoolC<true>{}, BoolC<true>{}, IntC<1>{});
-            kstep(kt + 2, BoolC<true>{}, BoolC<true>{}, IntC<2>{});
-            kstep(kt + 3, BoolC<true>{}, BoolC<true>{}, IntC<3>{});
+            kstep(kt, T, T, IntC<1>{}, F);
+            kstep(kt + 1, T, T, IntC<2>{}, F);
+            kstep(kt + 2, T, T, IntC<3>{}, F);
+            kstep(kt + 3, T, T, IntC<0>{}, F);
         }
-        for (; kt + STAGES - 1 < nk; ++kt) kstep(kt, BoolC<true>{}, BoolC<true>{}, IntC<-1>{});
-        for (; kt + 1 < nk; ++kt) kstep(kt, BoolC<false>{}, BoolC<true>{}, IntC<-1>{});
-        if (kt < nk) kstep(kt, BoolC<false>{}, BoolC<false>{}, IntC<-1>{});
+        for (; kt + STAGES - 1 < nk; ++kt) kstep(kt, T, T, IntC<-1>{}, F);
+        for (; kt + 1 < nk; ++kt) kstep(kt, F, T, IntC<-1>{}, F);
+        if (kt < nk) kstep(kt, F, F, IntC<-1>{}, F);
         __syncthreads();
         if constexpr (kSplit) {
             if (chunk >= 0) {  // a tail chunk: partial sums out, the fixup finishes the tile
