@@ -291,5 +291,11 @@ constexpr int kGemmBigN = MUON_GEMM_BIG_N;
 #define MUON_GEMM_BIG_MIN_TILES 512
 #endif
 constexpr int kGemmBigMinTiles = MUON_GEMM_BIG_MIN_TILES;
+// The Gram takes the big tile from this many big tiles on: on big tiles it reads X_c
+// (transposing LDS reads), so the cast and the Apply then skip the row-major X copy.
+#ifndef MUON_GEMM_BIG_MIN_TILES_GRAM
+#define MUON_GEMM_BIG_MIN_TILES_GRAM 128
+#endif
+constexpr int kGemmBigMinTilesGram = MUON_GEMM_BIG_MIN_TILES_GRAM;
 
 }  // namespace muon

@@ -9,7 +9,8 @@ library's C++:
   * tiles: the Gram and polynomial count the upper triangle of a [m, m] tile grid
     (diagonal included), the Apply every tile of [m, n]; each of the 8 XCDs takes a
     contiguous eighth of every matrix's tiles;
-  * tile width per stage: 256 when the stage has at least 512 such tiles; otherwise,
+  * tile width per stage: 256 when the stage has at least 512 such tiles (128 for the
+    Gram); otherwise,
     when every matrix of the group has the same K for the stage (n for the Gram, m for
     the polynomial and the Apply), 256 when the busiest XCD needs fewer rounds of them
     (32 per round, one block per compute unit) than of 128-wide tiles (64 per round, two
@@ -63,7 +64,7 @@ def shared_k(mats, stage):
 
 def tile_width(mats, stage):
     big = per_xcd(mats, stage, 256)
-    if sum(big) >= 512:
+    if sum(big) >= (128 if stage == "gram" else 512):
         return 256
     if shared_k(mats, stage) is None:
         return 128
