@@ -1,11 +1,14 @@
 // Newton-Schulz GEMM stage kernel template ("Muon is Scalable for LLM Training",
 // Sec. 2.1 Eq. 2: X <- a X + b (X X^T) X + c (X X^T)^2 X).
 //
-// Each iteration is three products, all of the form C[i][j] = sum_k P[i][k] Q[j][k]
-// with both operands K-contiguous in HBM:
-//   Gram  A = X X^T            P = Q = X_r ([m_p, n_p])      K = n_p   symmetric output
-//   Poly  P = aI + bA + cAA    P = Q = A   ([m_p, m_p])      K = m_p   symmetric (A = A^T)
-//   Apply X' = P X             P = P, Q = X_c ([n_p, m_p])   K = m_p   X'_r and X'_c out
+// Each iteration is three products, all of the form C[i][j] = sum_k P[i][k] Q[j][k]:
+//   Gram  A = X X^T            P = Q = X            K = n_p   symmetric output
+//   Poly  P = aI + bA + cAA    P = Q = A            K = m_p   symmetric (A = A^T)
+//   Apply X' = P X             P = P, Q = X_c       K = m_p   X'_c (and X'_r) out
+// X_c = X^T ([n_p, m_p]), A and P ([m_p, m_p]) are panel-blocked in HBM (kb_off): a K
+// step of a 256-row operand tile is one contiguous 16 KiB block. The big-tile Gram reads
+// X_c as K-major tiles (rows k) and transposes in the fragment reads; the small-tile
+// Gram reads the row-major copy X_r ([m_p, n_p]).
 // X' = a X + (b A + c A^2) X is computed as (a I + b A + c A^2) X: the polynomial's
 // epilogue adds a to the diagonal before its bf16 rounding, so the Apply is a plain
 // product whose epilogue reads no operand. (Measured with a CPU emulation of the bf16
@@ -17,24 +20,28 @@
 // applies Eq. 4 to W directly.
 //
 // Block: 256 threads = 2 x 2 waves, each wave a (BM/2) x (BN/2) sub-tile built from
-// v_mfma_f32_32x32x16_bf16 blocks (fp32 accumulation). K step 64 bf16 = 128-byte
-// LDS rows; the 16-byte chunk c of row r is stored at chunk position
-// c ^ ((r >> 1) & 7). The LDS serves a 16-byte-per-lane read 16 lanes (256 bytes,
-// all 64 banks) at a time; with this swizzle the 16 rows read by such a group land
-// on 16 distinct 16-byte bank groups (measured: a plain (r & 7) swizzle left half
-// of the LDS cycles in bank-conflict stalls).
+// v_mfma_f32_32x32x16_bf16 blocks (fp32 accumulation).
+//
+// Big tiles (256 x 256, kDirect): K step 32 in a ring of 4 LDS stages, three K steps
+// of loads in flight, one barrier per K step. The loads are buffer loads straight to
+// LDS (buffer_load_dwordx4 ... lds): a resource over the tile's panel in scalar
+// registers, one per-lane offset fixed for the whole K loop, a scalar offset per load;
+// each lane's 16 bytes land at LDS base + 16 * lane, so lane l fetches the logical chunk
+// that belongs at that (swizzled) position. The K loop is unrolled over the four ring
+// stages, so every LDS offset is a constant, and it issues no vector-ALU instruction:
+// measured on MI355X, vector-ALU work between MFMAs costs matrix-pipe throughput. K
+// step 0 starts the accumulators from a zero accumulator input.
+// Small tiles (128 x 128): K step 64 through registers (global -> VGPR -> LDS,
+// ds_write_b128), double-buffered, loads for step k + 1 in flight while step k computes.
+// K-contiguous LDS rows are swizzled: the 16-byte chunk c of row r sits at position
+// c ^ ((r >> s) & (chunks per row - 1)), so the 16 rows that a 16-lane group reads land
+// on distinct 16-byte bank groups (a plain (r & 7) swizzle left half of the LDS cycles
+// in bank-conflict stalls).
 //
 // Tile order: consecutive blocks (which run together on one XCD after the remap)
 // cover compact 2-D patches so that they share operand panels in L2: rectangular
 // stages walk groups of 8 tile-rows column by column, symmetric stages walk 4 x 4
 // super-tiles of the upper triangle.
-// Operand tiles are double-buffered in LDS, one barrier per K step. Two ways to
-// fill them:
-//   kDirect = false: global -> VGPR -> LDS (ds_write_b128), loads for step k+1 in
-//                    flight while step k computes;
-//   kDirect = true:  global_load_lds_dwordx4 (gfx950): each lane's 16 bytes land at
-//                    LDS base + 16 * lane, so lane l fetches the logical chunk that
-//                    belongs at that swizzled position.
 #pragma once
 
 #include "launch.hpp"

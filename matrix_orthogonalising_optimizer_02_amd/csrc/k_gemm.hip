@@ -4,7 +4,8 @@
 //   small: 128 x 128 block tile, register-staged loads, 64 KiB LDS, 2 blocks per CU;
 //   big:   256 x 256 block tile (each wave 128 x 128: half the LDS reads per MFMA of
 //          the small tile), K step 32 in a 4-deep ring of LDS stages filled by
-//          global_load_lds (three K steps of loads in flight), 128 KiB LDS, 1 block per CU.
+//          buffer loads straight to LDS (three K steps of loads in flight), 140 KiB LDS,
+//          1 block per CU.
 // The host picks, per stage, the big tile when the launch has enough big tiles to
 // fill the GPU, and the small one otherwise (small Gram matrices, small sets). A Gram,
 // polynomial or non-final Apply stage on big tiles whose XCDs would end on a short last
