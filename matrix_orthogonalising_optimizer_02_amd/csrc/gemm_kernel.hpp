@@ -824,7 +824,9 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
                 for (int it = 0; it < HN * WM / 8 / 64; ++it) {
                     const int c = it * 64 + lane, r = c / (WM / 8), k = c % (WM / 8);
                     const u32x4 val = *reinterpret_cast<const u32x4*>(lt + r * TSB + k * 8);
-                    *reinterpret_cast<u32x4*>(dst_t + kb_off(colh + r, row_base + k * 8, ld_t)) = val;
+                    // non-temporal: the outputs are read by the next launch, not by this
+                    // one, and kept out of the way of the operand slices in L2
+                    __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(dst_t + kb_off(colh + r, row_base + k * 8, ld_t)));
                 }
             }
             // direct rows: WM rows of HN values (HN / 8 chunks each); X'_r only when the
@@ -837,7 +839,7 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
                     // A and B are blocked; the Apply's X'_r is row-major
                     const int64_t o = (MODE == kModeApply) ? (int64_t)(row_base + r) * ld_d + colh + k * 8
                                                            : kb_off(row_base + r, colh + k * 8, ld_d);
-                    *reinterpret_cast<u32x4*>(dst_d + o) = val;
+                    __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(dst_d + o));
                 }
             }
         } else if (d.tall) {
