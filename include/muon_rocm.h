@@ -144,8 +144,10 @@ int muon_workspace_bytes(const int64_t* rows, const int64_t* cols, int32_t count
  *   [1 .. 16]  their indices into rows / cols, -1 past that count;
  *   then 17 values for each of the Gram, the polynomial, the Apply of iterations
  *   1 .. N-1 and the last Apply, in that order: the tile width (128 or 256), then for
- *   XCD 0 .. 7 the number of its last round's tiles that run as K chunks and the
- *   number of chunks (0 and 1 where the XCD does not split).
+ *   XCD 0 .. 7 the number of its tiles that run as K chunks and the number of chunks
+ *   (0 and 1 where the XCD does not split). A positive count h means the last h tiles
+ *   of its sequence (tail split); a negative one, -h, its first h (head split, for a
+ *   stage whose tiles fit one round and whose matrices differ in K).
  * capacity 0 only reports *groups (out may then be NULL).
  * Errors: INVALID_ARG (NULL groups, count < 0, NULL rows / cols with count > 0,
  * negative dims, capacity < 0, NULL out with capacity > 0, capacity below the

@@ -168,8 +168,10 @@ PLAN_STAGES = ("gram", "poly", "apply", "apply_final")
 
 def ns5_plan(shapes: Sequence[Sequence[int]]):
     """The Newton-Schulz GEMM plan the library uses for these shapes (host only): one
-    dict per group with the matrices' indices and, per stage, (tile width, {XCD: (tiles
-    of its last round run as K chunks, chunks)}) for the XCDs that split."""
+    dict per group with the matrices' indices and, per stage, (tile width, {XCD: (split
+    tiles, chunks)}) for the XCDs that split. Split tiles > 0: that many tiles of the
+    XCD's last round run as K chunks (tail split); < 0: its first -h tiles do (head
+    split of a one-round stage with mixed K)."""
     lib = load_library()
     n = len(shapes)
     rows = (ctypes.c_int64 * max(n, 1))(*[int(s[0]) for s in shapes])
@@ -185,7 +187,7 @@ def ns5_plan(shapes: Sequence[Sequence[int]]):
         rec = {"indices": [int(v) for v in r[1:1 + r[0]]]}
         for st, name in enumerate(PLAN_STAGES):
             q = r[17 + 17 * st:34 + 17 * st]
-            rec[name] = (int(q[0]), {x: (int(q[1 + 2 * x]), int(q[2 + 2 * x])) for x in range(8) if q[1 + 2 * x] > 0})
+            rec[name] = (int(q[0]), {x: (int(q[1 + 2 * x]), int(q[2 + 2 * x])) for x in range(8) if q[1 + 2 * x] != 0})
         groups.append(rec)
     return groups
 

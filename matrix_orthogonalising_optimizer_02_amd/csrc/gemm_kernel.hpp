@@ -226,9 +226,11 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
     // K differ, and neighbouring tiles (shared operand panels) in the same L2. Blocks
     // left without a tile (the grid is 8 x the largest per-XCD count) exit here.
     constexpr bool kSym = (MODE == kModeGram || MODE == kModePoly);
-    // Tail split (Gram, polynomial and non-final Apply on the direct-load tile): the
-    // XCD's blocks from xfull[x] on are chunk c of its tail tile xfull[x] + u / S,
-    // u = block - xfull[x].
+    // Split tiles (Gram, polynomial and non-final Apply on the direct-load tile): the
+    // XCD's tiles xfull[x] .. xfull[x] + xtail[x] - 1 run as S = xsplit[x] chunks of K
+    // each. Its blocks from xfull[x] on, u = block - xfull[x], are chunk u % S of tile
+    // xfull[x] + u / S while u < xtail[x] S, then the tiles after the split ones, whole.
+    // Tail split: the split tiles end the sequence. Head split: xfull[x] = 0.
     constexpr bool kSplit = (kSym || MODE == kModeApply) && Cfg::kDirect && kSplitOK;
     int chunk = -1, nsplit = 1, unit = 0;
     int gi = -1, local = 0;
@@ -238,11 +240,15 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
         if constexpr (kSplit) {
             if (sl >= args.xfull[x]) {
                 const int u = sl - args.xfull[x];
-                nsplit = args.xsplit[x];
-                if (u >= args.xtail[x] * nsplit) return;
-                chunk = u % nsplit;
-                sl = args.xfull[x] + u / nsplit;
-                unit = args.xpbase[x] + u;
+                const int nt = args.xtail[x], S = args.xsplit[x];
+                if (u < nt * S) {
+                    nsplit = S;
+                    chunk = u % S;
+                    sl = args.xfull[x] + u / S;
+                    unit = args.xpbase[x] + u;
+                } else {
+                    sl = args.xfull[x] + nt + (u - nt * S);
+                }
             }
         }
         xcd_slot(args, x, sl, gi, local);

@@ -36,15 +36,15 @@ __global__ __launch_bounds__(256, (Cfg::kLdsBytes > 80 * 1024) ? 1 : 2) void k_n
     ns_gemm_tile<MODE, Cfg, SPLIT>(args, smem);
 }
 
-// Fixup of the split tail tiles of a stage (big tiles: 2 x 2 waves of 4 x 4 blocks of
-// 32 x 32). Each thread takes 4 consecutive accumulator lanes of one wave and register
-// index of one tail tile, adds the tile's chunks in chunk order and applies the stage's
+// Fixup of the split tiles of a stage, tail or head split (big tiles: 2 x 2 waves of 4 x 4
+// blocks of 32 x 32). Each thread takes 4 consecutive accumulator lanes of one wave and
+// register index of one split tile, adds the tile's chunks in chunk order and applies the stage's
 // epilogue arithmetic, as the tile epilogue does:
 //   Gram        A = s2 acc, bf16 at (i, j) and, off the diagonal, at (j, i);
 //   polynomial  P = a [i == j < m] + b A + c acc (A read at (j, i)), stored the same way;
 //   Apply       X' = s1 acc, bf16 into X'_c at (j, i) and into the row-major X'_r at
 //               (i, j) when the next Gram reads it.
-// kTailUnitFloats / 1024 blocks per tail tile.
+// kTailUnitFloats / 1024 blocks per split tile.
 template <int MODE>
 __global__ __launch_bounds__(256) void k_ns_tail_fix(NsArgs args) {
     using Cfg = BigCfg;

@@ -74,13 +74,14 @@ struct NsDesc {
     float* part;           // final modes, optional: [ntiles * 4] per-wave sums of O^2
 };
 
-// Gram, polynomial and non-final Apply stages on big tiles may split the last round of
-// tiles of an XCD: its
-// sequence of tiles ends with xtail[x] tiles that run as xsplit[x] chunks of K each
-// (blocks xfull[x] .. xfull[x] + xtail[x] * xsplit[x] - 1 of the XCD), writing fp32
-// partial tiles (kTailUnitFloats each, accumulator order) at tail + (xpbase[x] + u) *
-// kTailUnitFloats. A fixup launch of sum(xtail) blocks adds each tile's chunks in chunk
-// order and runs the stage's epilogue. tail == nullptr: no split.
+// Gram, polynomial and non-final Apply stages on big tiles may split tiles of an XCD in
+// K: tiles xfull[x] .. xfull[x] + xtail[x] - 1 of its sequence run as xsplit[x] chunks
+// of K each (blocks xfull[x] .. xfull[x] + xtail[x] * xsplit[x] - 1 of the XCD; any
+// tiles after them follow, whole), writing fp32 partial tiles (kTailUnitFloats each,
+// accumulator order) at tail + (xpbase[x] + u) * kTailUnitFloats. The tail split takes
+// the last round's tiles; the head split (xfull[x] = 0) the first, longest tiles of a
+// one-round stage with mixed K. A fixup launch of sum(xtail) tiles adds each tile's
+// chunks in chunk order and runs the stage's epilogue. tail == nullptr: no split.
 #ifndef MUON_GEMM_TAIL_SPLIT
 #define MUON_GEMM_TAIL_SPLIT 1
 #endif

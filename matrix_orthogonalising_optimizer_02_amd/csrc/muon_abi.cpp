@@ -125,7 +125,7 @@ enum SplitStage : int { kStageGram = 0, kStagePoly = 1, kStageApply = 2 };
 // the Apply). Returns the stage's K in 32-wide steps when every matrix of the group has
 // the same K (Gram: n_p; polynomial and Apply: m_p), else 0: with mixed K the last tiles
 // of an XCD are its shortest ones and splitting them was measured to cost more than it
-// saves.
+// saves (such a stage may take the head split instead).
 int64_t xcd_counts(const GroupPlan& gp, int stage, int64_t cnt[8]) {
     for (int x = 0; x < 8; ++x) cnt[x] = 0;
     int64_t k = -1;
@@ -138,6 +138,88 @@ int64_t xcd_counts(const GroupPlan& gp, int stage, int64_t cnt[8]) {
         else if (k != kp) k = 0;
     }
     return k > 0 ? k / 32 : 0;
+}
+
+// Head split of a stage on big tiles whose matrices have different K and whose tiles all
+// fit one round (at most kCusPerXcd per XCD): the XCD's tiles all start together, so the
+// stage lasts as long as its longest tile, the first ones of its sequence (the group runs
+// longest K first). XCD x runs its first h tiles as S chunks of K each (blocks 0 .. h S - 1,
+// its other tiles after them), within one round: h S + cnt - h <= kCusPerXcd, and every
+// split tile at least S units of 256 of K long. Its longest block is then max(ceil(k_i / S)
+// over the split tiles, k_i over the others), k in units of 256. The stage's target is the
+// largest over the XCDs of the smallest such value; each XCD then takes, among the (h, S)
+// that reach the target, the one with the fewest partial tiles (then the fewest chunks).
+// Taken, like the tail split, when the K steps saved on the longest XCD beat the
+// partial-tile cost. Measured on the H = 2048 DiT block's Gram (the odd XCDs' 25 tiles of
+// 48 to 8 units: 48 -> 32). Returns the number of partial tiles (0: no split).
+int64_t head_split(const GroupPlan& gp, int stage, NsArgs* na) {
+    std::vector<int64_t> ks[8];
+    for (const MatPlan& p : gp.mats) {
+        const int64_t t = p.m_p / kGemmBigM;
+        const int64_t T = stage == kStageApply ? t * (p.n_p / kGemmBigN) : t * (t + 1) / 2;
+        const int64_t k = (stage == kStageGram ? p.n_p : p.m_p) / 256;
+        for (int x = 0; x < 8; ++x)
+            ks[x].insert(ks[x].end(), size_t(((x + 1) * T >> 3) - (x * T >> 3)), k);
+    }
+    // per XCD: the longest block of a split of the first h tiles into S chunks
+    auto longest = [&](const std::vector<int64_t>& v, int64_t h, int64_t S) {
+        int64_t l = 0;
+        for (int64_t i = 0; i < int64_t(v.size()); ++i)
+            l = std::max(l, i < h ? (v[size_t(i)] + S - 1) / S : v[size_t(i)]);
+        return l;
+    };
+    auto fits = [&](const std::vector<int64_t>& v, int64_t h, int64_t S) {
+        if (h * S + int64_t(v.size()) - h > kCusPerXcd) return false;
+        for (int64_t i = 0; i < h; ++i)
+            if (v[size_t(i)] < S) return false;
+        return true;
+    };
+    int64_t before = 0, target = 0;
+    for (int x = 0; x < 8; ++x) {
+        if (int64_t(ks[x].size()) > kCusPerXcd) return 0;
+        const int64_t l0 = longest(ks[x], 0, 1);
+        int64_t best = l0;
+        for (int64_t S = 2; S <= kTailMaxSplit; ++S)
+            for (int64_t h = 1; h <= int64_t(ks[x].size()) && fits(ks[x], h, S); ++h)
+                best = std::min(best, longest(ks[x], h, S));
+        before = std::max(before, l0);
+        target = std::max(target, best);
+    }
+    int64_t H[8], SS[8], units = 0;
+    for (int x = 0; x < 8; ++x) {
+        H[x] = 0;
+        SS[x] = 1;
+        if (longest(ks[x], 0, 1) <= target) continue;
+        for (int64_t S = 2; S <= kTailMaxSplit; ++S)
+            for (int64_t h = 1; h <= int64_t(ks[x].size()) && fits(ks[x], h, S); ++h)
+                if (longest(ks[x], h, S) <= target && (H[x] == 0 || h * S < H[x] * SS[x])) {
+                    H[x] = h;
+                    SS[x] = S;
+                }
+        units += H[x] * SS[x];
+    }
+    const double saved = double((before - target) * 8) * kTailStepUs;
+    if (units == 0 || saved <= double(units) * kTailUnitUs + kTailFixedUs) return 0;
+    if (na) {
+        int64_t base = 0;
+        for (int x = 0; x < 8; ++x) {
+            na->xfull[x] = 0;
+            na->xtail[x] = int32_t(H[x]);
+            na->xsplit[x] = int32_t(SS[x]);
+            na->xpbase[x] = int32_t(base);
+            base += H[x] * SS[x];
+        }
+    }
+    return units;
+}
+
+// The split of a stage on big tiles: the tail split when its matrices share K, else the
+// head split. *head (optional) tells which.
+int64_t split_plan(const GroupPlan& gp, int stage, NsArgs* na, bool* head = nullptr) {
+    int64_t cnt[8];
+    const int64_t ks = xcd_counts(gp, stage, cnt);
+    if (head) *head = ks == 0;
+    return ks ? tail_split(cnt, ks, na) : head_split(gp, stage, na);
 }
 
 // Big tiles of a stage, the first test of choose_tile.
@@ -264,12 +346,10 @@ int make_plan(const int64_t* rows, const int64_t* cols, int32_t count, Plan* pla
             return fail(MUON_ERR_TOO_LARGE, "a launch would exceed 2^31 workgroups");
         if (kGemmTailSplit) {
             // the partial-tile region serves whichever stage splits the most tiles
-            int64_t cnt[8];
             gp.tail_units = 0;
             for (int st = kStageGram; st <= kStageApply; ++st) {
                 if (choose_tile(gp, st != kStageApply, st) != kTileBig) continue;
-                const int64_t ks = xcd_counts(gp, st, cnt);
-                if (ks) gp.tail_units = std::max(gp.tail_units, tail_split(cnt, ks, nullptr));
+                gp.tail_units = std::max(gp.tail_units, split_plan(gp, st, nullptr));
             }
             if (gp.tail_units > 0) {
                 gp.tail = ns;
@@ -434,7 +514,7 @@ struct IoPtrs {
 // tiles into the workspace's partial-tile region. describe: plan that split without a
 // workspace (ns5_plan reads xtail / xsplit; na.tail stays NULL).
 GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym, char* ws = nullptr, int stage = kStageGram,
-                    bool describe = false) {
+                    bool describe = false, bool* head = nullptr) {
     const int ng = int(gp.mats.size());
     const GemmTile tile = choose_tile(gp, sym, stage);
     const int64_t bm = tile == kTileBig ? kGemmBigM : kGemmSmall;
@@ -466,12 +546,12 @@ GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym, char* ws = nullpt
     na.fix_total = 0;
     if (tile == kTileBig && (ws != nullptr || describe) && gp.tail_units > 0) {
         int64_t cnt[8], fix = 0, longest = 0;
-        const int64_t ks = xcd_counts(gp, stage, cnt);
-        const int64_t units = ks ? tail_split(cnt, ks, &na) : 0;
+        xcd_counts(gp, stage, cnt);
+        const int64_t units = split_plan(gp, stage, &na, head);
         if (units > 0 && units <= gp.tail_units) {
             for (int x = 0; x < 8; ++x) {
                 fix += na.xtail[x];
-                longest = std::max<int64_t>(longest, int64_t(na.xfull[x]) + int64_t(na.xtail[x]) * na.xsplit[x]);
+                longest = std::max<int64_t>(longest, cnt[x] + int64_t(na.xtail[x]) * (na.xsplit[x] - 1));
             }
             na.tail = ws ? reinterpret_cast<float*>(ws + gp.tail) : nullptr;
             na.fix_total = int32_t(fix);
@@ -1086,11 +1166,12 @@ MUON_API int ns5_plan(const int64_t* rows, const int64_t* cols, int32_t count, i
         const bool split[4] = {true, true, true, false};
         for (int st = 0; st < 4; ++st) {
             NsArgs na{};
-            const GemmTile tile = plan_tiles(gp, na, sym[st], nullptr, stage[st], split[st]);
+            bool head = false;
+            const GemmTile tile = plan_tiles(gp, na, sym[st], nullptr, stage[st], split[st], &head);
             int32_t* q = r + 1 + kMaxGroup + st * 17;
             q[0] = tile == kTileBig ? int32_t(kGemmBigM) : int32_t(kGemmSmall);
             for (int x = 0; x < 8; ++x) {
-                q[1 + 2 * x] = na.fix_total > 0 ? na.xtail[x] : 0;
+                q[1 + 2 * x] = na.fix_total > 0 ? (head ? -na.xtail[x] : na.xtail[x]) : 0;
                 q[2 + 2 * x] = na.fix_total > 0 ? na.xsplit[x] : 1;
             }
         }

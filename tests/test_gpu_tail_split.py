@@ -1,4 +1,4 @@
-"""GPU parity of the split tail of the NS5 GEMM stages.
+"""GPU parity of the split tiles of the NS5 GEMM stages: the tail split and the head split.
 
 When a group's Gram, polynomial or non-final Apply stage runs on 256-wide tiles and
 every matrix of the group has the same K for it, an XCD whose tile count leaves a last
@@ -20,6 +20,13 @@ Four sets exercise it:
     tiles) against three of 128-wide ones (132), so the Gram and polynomial run on
     256-wide tiles and every XCD splits its last 2 (from the second matrix) in 8
     chunks; the Apply (64 tiles per XCD) does not split.
+When the group's matrices differ in K and every XCD's tiles fit one round, the XCD
+instead runs its first (longest) tiles as K chunks, the head split. Two sets exercise it:
+  * [2048, 8192] and 3 x [2048, 2048] (144 upper tiles; K 32 and 8 units of 256): every
+    XCD runs its 4 or 5 tiles of the first matrix as 3 chunks of 10 to 11 units (uneven
+    chunks), its longest block 32 -> 11 units;
+  * [6144, 3072] and [3072, 3072] (156 upper tiles; K 24 and 12 units): XCDs run their 9
+    or 10 tiles of the first matrix as 2 chunks, 24 -> 12 units.
 The matrices with split tiles and the first one are checked against the float64
 oracle's Newton-Schulz at the bf16 tolerance, and each call is repeated to check
 that the fixed-order chunk sums make it bitwise repeatable. The library's plan
@@ -87,10 +94,37 @@ def test_split_tail_tiles_vs_oracle_and_repeatable(torch_dev, case):
         log(f"  matrix {i} {shapes[i]}: rel err {err:.3e}, worst line {line:.3e}")
 
 
+HEAD_CASES = [
+    ([(2048, 8192)] + [(2048, 2048)] * 3, [0, 3], {x: (-4 - (x & 1), 3) for x in range(8)}),
+    ([(6144, 3072), (3072, 3072)], [0, 1], {x: (-9 if x in (0, 4) else -10, 2) for x in range(8)}),
+]
+
+
+@pytest.mark.parametrize("case", range(len(HEAD_CASES)))
+def test_split_head_tiles_vs_oracle_and_repeatable(torch_dev, case):
+    torch, dev = torch_dev
+    shapes, checked, split = HEAD_CASES[case]
+    plan = B.ns5_plan(shapes)
+    assert len(plan) == 1 and plan[0]["gram"] == (256, split)
+    xs = [WL.host_normal(17 + case, WL.ROLE_G, i, s, 1e-3) for i, s in enumerate(shapes)]
+    ins = [torch.from_numpy(x.astype(np.float32)).to(dev) for x in xs]
+    log(f"ns5_batched: {shapes}, Gram head split {split}, polynomial {plan[0]['poly']}, Apply {plan[0]['apply']}")
+    outs = B.ns5_batched(ins)
+    outs2 = B.ns5_batched(ins)
+    torch.cuda.synchronize()
+    for i, (o, o2) in enumerate(zip(outs, outs2)):
+        assert torch.equal(o, o2), f"matrix {i}: two calls differ"
+    for i in checked:
+        ref = O.newton_schulz(xs[i].astype(np.float32).astype(np.float64))
+        oh = outs[i].detach().cpu().numpy().astype(np.float64)
+        err, line = assert_ns_close(oh, ref, shapes[i], i)
+        log(f"  matrix {i} {shapes[i]}: rel err {err:.3e}, worst line {line:.3e}")
+
+
 def random_big_sets(count=6, seed=20241202):
     """Seeded sets on 256-wide tiles: m from 2048 to 3072, n = m, m + 256 or 2 m, random
     orientation, 1 to 16 matrices of one or two shapes; a set is kept when the library's
-    plan splits a tail in some stage or takes 256-wide tiles for a stage with fewer than
+    plan splits tiles (tail or head) in some stage or takes 256-wide tiles for a stage with fewer than
     512 of them (the fewer-rounds rule)."""
     rng = np.random.default_rng(seed)
     out = []

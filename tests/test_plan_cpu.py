@@ -19,7 +19,16 @@ library's C++:
     round holds r <= 16 tiles runs them as S = min(8, 32 // r, K / 256) chunks of K
     (S >= 2), taken only when (1 - 1 / S_min) of a tile's K steps at 0.86 us each exceeds
     0.13 us per partial tile plus 10 us; the partial-tile region is sized for the stage
-    that splits the most tiles, and the last Apply never splits.
+    that splits the most tiles, and the last Apply never splits;
+  * head split, for a stage on 256-wide tiles whose matrices do not share K and whose
+    XCDs hold at most 32 tiles each: an XCD may run its first h tiles (K units of 256
+    k_0, k_1, ...) as S in 2..8 chunks each, when h S plus its other tiles stay within
+    32 and each split tile has at least S units; its longest block is then the largest
+    of ceil(k_i / S) over the split tiles and k_i over the rest. The target is the
+    largest over the XCDs of each one's best; each XCD above it takes the (h, S) that
+    reaches it with the fewest partial tiles h S, then the smallest S; taken when the
+    units saved on the longest XCD, 8 K steps at 0.86 us each, beat the same partial
+    cost. Reported as (-h, S).
 Sets: the benchmark workloads, the GPU tests' sets, and a seeded sweep of random sets.
 """
 import ctypes
@@ -94,6 +103,43 @@ def tail_split(mats, stage):
     return units, out
 
 
+def head_split(mats, stage):
+    """(partial tiles, {XCD: (-h, chunks)}) of a one-round stage with mixed K."""
+    seqs = [[] for _ in range(XCDS)]
+    for m, n in mats:
+        k = (n if stage == "gram" else m) // 256
+        for x, c in enumerate(per_xcd([(m, n)], stage, 256)):
+            seqs[x] += [k] * c
+    if max(len(v) for v in seqs) > CUS:
+        return 0, {}
+
+    def options(v):
+        # (longest block, partial tiles, S, h) of every allowed split, and no split
+        yield max(v, default=0), 0, 1, 0
+        for S in range(2, 9):
+            for h in range(1, len(v) + 1):
+                if h * S + len(v) - h > CUS or min(v[:h]) < S:
+                    break
+                yield max([ceil_div(k, S) for k in v[:h]] + v[h:]), h * S, S, h
+
+    before = max(max(v, default=0) for v in seqs)
+    target = max(min(o[0] for o in options(v)) for v in seqs)
+    out = {}
+    for x, v in enumerate(seqs):
+        if max(v, default=0) <= target:
+            continue
+        _, units, S, h = min((o for o in options(v) if o[0] <= target and o[1] > 0), key=lambda o: (o[1], o[2]))
+        out[x] = (-h, S)
+    units = sum(-h * S for h, S in out.values())
+    if not out or (before - target) * 8 * 0.86 <= units * 0.13 + 10.0:
+        return 0, {}
+    return units, out
+
+
+def split_of(mats, stage):
+    return tail_split(mats, stage) if shared_k(mats, stage) is not None else head_split(mats, stage)
+
+
 def expected_plan(shapes):
     work = []
     for i, (a, b) in enumerate(shapes):
@@ -106,7 +152,7 @@ def expected_plan(shapes):
         grp = work[g0:g0 + GROUP]
         mats = [(w[0], w[1]) for w in grp]
         tiles = {st: tile_width(mats, st) for st in ("gram", "poly", "apply")}
-        splits = {st: tail_split(mats, st) if tiles[st] == 256 else (0, {}) for st in tiles}
+        splits = {st: split_of(mats, st) if tiles[st] == 256 else (0, {}) for st in tiles}
         rec = {"indices": [w[4] for w in grp]}
         for st in ("gram", "poly", "apply"):
             rec[st] = (tiles[st], splits[st][1])
@@ -147,6 +193,30 @@ def test_plan_of_random_sets():
         assert B.ns5_plan(shapes) == want, (trial, shapes)
         splits += sum(1 for g in want for st in ("gram", "poly", "apply") if g[st][1])
     assert splits > 20  # the sweep exercises the split rule, not only the tile rule
+
+
+def test_plan_of_random_mixed_k_sets():
+    """Seeded random sets that share m but differ in n (the Gram's K), few enough tiles
+    for one round: the sets the head split is for. The sweep must take it often, with
+    more than one chunk count."""
+    _lib_or_skip()
+    rng = np.random.default_rng(20241203)
+    heads, chunks = 0, set()
+    for trial in range(300):
+        m = int(rng.choice([1024, 1536, 2048, 2304, 2560, 3072, 3328]))
+        ns = [int(rng.choice([1, 2, 3, 4, 6, 8])) * m + int(rng.choice([0, 0, 100])) for _ in range(int(rng.integers(2, 4)))]
+        shapes = []
+        for _ in range(int(rng.integers(2, 9))):
+            n = ns[int(rng.integers(0, len(ns)))]
+            shapes.append((m, n) if rng.random() < 0.5 else (n, m))
+        want = expected_plan(shapes)
+        assert B.ns5_plan(shapes) == want, (trial, shapes)
+        for g in want:
+            for h, S in g["gram"][1].values():
+                if h < 0:
+                    heads += 1
+                    chunks.add(S)
+    assert heads > 50 and len(chunks) >= 2
 
 
 def test_record_size_matches_the_header():
