@@ -184,13 +184,14 @@ __device__ __forceinline__ void tri_tile(int local, int T, int& ti, int& tj) {
 }
 
 // Slot `sl` of XCD x -> (matrix gi, tile index local): every XCD walks the group's
-// matrices in order and takes one contiguous eighth of each one's tiles. gi = -1 when
-// the XCD has fewer slots.
+// matrices in order and takes one contiguous eighth of each one's tiles, eighth
+// (x + rot) & 7 of matrix g (the host picks rot to balance the XCDs). gi = -1 when the
+// XCD has fewer slots.
 __device__ __forceinline__ void xcd_slot(const NsArgs& args, int x, int sl, int& gi, int& local) {
     gi = -1;
     for (int g = 0; g < args.n; ++g) {
-        const int T = args.d[g].ntiles;
-        const int lo = (x * T) >> 3, cnt = (((x + 1) * T) >> 3) - lo;
+        const int T = args.d[g].ntiles, j = (x + args.d[g].rot) & 7;
+        const int lo = (j * T) >> 3, cnt = (((j + 1) * T) >> 3) - lo;
         if (sl < cnt) {
             gi = g;
             local = lo + sl;
@@ -222,9 +223,10 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
 
     // Blocks are dealt round-robin over the 8 XCDs (block b runs on XCD b % 8). Every
     // XCD walks the group's matrices in order (longest K first) and takes one contiguous
-    // eighth of each matrix's tile sequence: equal work per XCD even when the matrices'
-    // K differ, and neighbouring tiles (shared operand panels) in the same L2. Blocks
-    // left without a tile (the grid is 8 x the largest per-XCD count) exit here.
+    // eighth of each matrix's tile sequence, the eighths rotated per matrix to balance
+    // the XCDs' work even when the matrices' K differ, and neighbouring tiles (shared
+    // operand panels) in the same L2. Blocks left without a tile (the grid is 8 x the
+    // largest per-XCD count) exit here.
     constexpr bool kSym = (MODE == kModeGram || MODE == kModePoly);
     // Split tiles (Gram, polynomial and non-final Apply on the direct-load tile): the
     // XCD's tiles xfull[x] .. xfull[x] + xtail[x] - 1 run as S = xsplit[x] chunks of K

@@ -70,6 +70,7 @@ struct NsDesc {
     int32_t tall;
     int32_t ntiles;        // tiles of this matrix in the stage
     int32_t tiles;         // symmetric: tiles per side; rectangular: tiles along n
+    int32_t rot;           // XCD x takes eighth (x + rot) & 7 of this matrix's tiles
     float upd_coef;        // lr * (the update's direction scale), fused Eq. 4 / 5 update
     float* part;           // final modes, optional: [ntiles * 4] per-wave sums of O^2
 };

@@ -120,24 +120,76 @@ int64_t tail_split(const int64_t cnt[8], int64_t ksteps, NsArgs* na) {
 
 enum SplitStage : int { kStageGram = 0, kStagePoly = 1, kStageApply = 2 };
 
-// Big tiles per XCD of a stage of a group (each XCD takes a contiguous eighth of every
-// matrix's tiles: upper-triangle tiles for the Gram and polynomial, all tiles of X' for
-// the Apply). Returns the stage's K in 32-wide steps when every matrix of the group has
-// the same K (Gram: n_p; polynomial and Apply: m_p), else 0: with mixed K the last tiles
-// of an XCD are its shortest ones and splitting them was measured to cost more than it
-// saves (such a stage may take the head split instead).
-int64_t xcd_counts(const GroupPlan& gp, int stage, int64_t cnt[8]) {
-    for (int x = 0; x < 8; ++x) cnt[x] = 0;
+// Tiles of eighth j of a sequence of T tiles.
+inline int64_t eighth(int64_t T, int64_t j) { return ((j + 1) * T >> 3) - (j * T >> 3); }
+
+// Tiles of matrix p in a stage on `tile`-wide tiles (upper-triangle tiles for the Gram
+// and polynomial, all tiles of X' for the Apply) and their K in units of 256 (Gram: n_p;
+// polynomial and Apply: m_p).
+int64_t stage_tiles(const MatPlan& p, int stage, int64_t tile) {
+    const int64_t t = p.m_p / tile;
+    return stage == kStageApply ? t * (p.n_p / tile) : t * (t + 1) / 2;
+}
+int64_t stage_k(const MatPlan& p, int stage) { return (stage == kStageGram ? p.n_p : p.m_p) / 256; }
+
+// How a stage's tiles are dealt to the 8 XCDs. Each XCD takes one contiguous eighth of
+// every matrix's tile sequence, so neighbouring tiles, which share operand panels, meet
+// in its L2: eighth (x + rot) & 7 goes to XCD x. Eighths of a sequence whose length is
+// not a multiple of 8 differ by one tile. The balanced deal gives each matrix, in group
+// order, the rotation that leaves the XCDs' loads (tiles x K) with the smallest sum of
+// squares, the first one on a tie; the plain deal rotates nothing, so the same XCDs
+// take the larger eighth of every matrix (the 16-matrix [2048, 8192] bucket's Gram: 80
+// tiles on four XCDs, 64 on the others).
+struct XcdDeal {
+    int32_t rot[kMaxGroup];
+    int64_t cnt[8];
+};
+XcdDeal xcd_deal(const GroupPlan& gp, int stage, int64_t tile, bool balance) {
+    XcdDeal d{};
+    int64_t load[8] = {0};
+    for (size_t g = 0; g < gp.mats.size(); ++g) {
+        const int64_t T = stage_tiles(gp.mats[g], stage, tile), k = stage_k(gp.mats[g], stage);
+        int best_r = 0;
+        int64_t best = -1;
+        for (int r = 0; balance && r < 8; ++r) {
+            int64_t v = 0;
+            for (int x = 0; x < 8; ++x) {
+                const int64_t l = load[x] + eighth(T, (x + r) & 7) * k;
+                v += l * l;
+            }
+            if (best < 0 || v < best) {
+                best = v;
+                best_r = r;
+            }
+        }
+        d.rot[g] = best_r;
+        for (int x = 0; x < 8; ++x) {
+            const int64_t e = eighth(T, (x + best_r) & 7);
+            d.cnt[x] += e;
+            load[x] += e * k;
+        }
+    }
+    return d;
+}
+
+// Per XCD, the K (units of 256) of each big tile it takes, in order.
+void xcd_seqs(const GroupPlan& gp, int stage, const XcdDeal& deal, std::vector<int64_t> ks[8]) {
+    for (int x = 0; x < 8; ++x) ks[x].clear();
+    for (size_t g = 0; g < gp.mats.size(); ++g) {
+        const int64_t T = stage_tiles(gp.mats[g], stage, kGemmBigM), k = stage_k(gp.mats[g], stage);
+        for (int x = 0; x < 8; ++x) ks[x].insert(ks[x].end(), size_t(eighth(T, (x + deal.rot[g]) & 7)), k);
+    }
+}
+
+// The stage's K in 32-wide steps when every matrix of the group has the same K, else 0.
+int64_t shared_ksteps(const GroupPlan& gp, int stage) {
     int64_t k = -1;
     for (const MatPlan& p : gp.mats) {
-        const int64_t t = p.m_p / kGemmBigM;
-        const int64_t T = stage == kStageApply ? t * (p.n_p / kGemmBigN) : t * (t + 1) / 2;
-        for (int x = 0; x < 8; ++x) cnt[x] += ((x + 1) * T >> 3) - (x * T >> 3);
-        const int64_t kp = stage == kStageGram ? p.n_p : p.m_p;
+        const int64_t kp = stage_k(p, stage);
         if (k < 0) k = kp;
         else if (k != kp) k = 0;
     }
-    return k > 0 ? k / 32 : 0;
+    return k > 0 ? k * 8 : 0;
 }
 
 // Head split of a stage on big tiles whose matrices have different K and whose tiles all
@@ -151,16 +203,9 @@ int64_t xcd_counts(const GroupPlan& gp, int stage, int64_t cnt[8]) {
 // that reach the target, the one with the fewest partial tiles (then the fewest chunks).
 // Taken, like the tail split, when the K steps saved on the longest XCD beat the
 // partial-tile cost. Measured on the H = 2048 DiT block's Gram (the odd XCDs' 25 tiles of
-// 48 to 8 units: 48 -> 32). Returns the number of partial tiles (0: no split).
-int64_t head_split(const GroupPlan& gp, int stage, NsArgs* na) {
-    std::vector<int64_t> ks[8];
-    for (const MatPlan& p : gp.mats) {
-        const int64_t t = p.m_p / kGemmBigM;
-        const int64_t T = stage == kStageApply ? t * (p.n_p / kGemmBigN) : t * (t + 1) / 2;
-        const int64_t k = (stage == kStageGram ? p.n_p : p.m_p) / 256;
-        for (int x = 0; x < 8; ++x)
-            ks[x].insert(ks[x].end(), size_t(((x + 1) * T >> 3) - (x * T >> 3)), k);
-    }
+// 48 to 8 units: 48 -> 32). Returns the number of partial tiles (0: no split); *span
+// (optional) receives the longest block in units of 256 of K.
+int64_t head_split(const std::vector<int64_t> ks[8], NsArgs* na, int64_t* span = nullptr) {
     // per XCD: the longest block of a split of the first h tiles into S chunks
     auto longest = [&](const std::vector<int64_t>& v, int64_t h, int64_t S) {
         int64_t l = 0;
@@ -185,6 +230,7 @@ int64_t head_split(const GroupPlan& gp, int stage, NsArgs* na) {
         before = std::max(before, l0);
         target = std::max(target, best);
     }
+    if (span) *span = before;
     int64_t H[8], SS[8], units = 0;
     for (int x = 0; x < 8; ++x) {
         H[x] = 0;
@@ -200,6 +246,7 @@ int64_t head_split(const GroupPlan& gp, int stage, NsArgs* na) {
     }
     const double saved = double((before - target) * 8) * kTailStepUs;
     if (units == 0 || saved <= double(units) * kTailUnitUs + kTailFixedUs) return 0;
+    if (span) *span = target;
     if (na) {
         int64_t base = 0;
         for (int x = 0; x < 8; ++x) {
@@ -213,13 +260,78 @@ int64_t head_split(const GroupPlan& gp, int stage, NsArgs* na) {
     return units;
 }
 
-// The split of a stage on big tiles: the tail split when its matrices share K, else the
-// head split. *head (optional) tells which.
+// Modelled time of a stage on big tiles under a deal, in hundredths of a microsecond:
+// the busiest XCD's span in K steps at kTailStepUs each, plus the partial-tile cost of
+// the split the planner takes under that deal. An XCD runs its blocks on kCusPerXcd
+// compute units, each block on the first one free, in order: with one K the span is
+// q K plus the last round's (chunked) tiles; with mixed K and one round it is the
+// longest block; with mixed K and more rounds it is found by that list schedule.
+int64_t deal_cost(const GroupPlan& gp, int stage, const XcdDeal& deal) {
+    constexpr int64_t kStep = 86, kUnit = 13, kFixed = 1000;  // kTailStepUs, kTailUnitUs, kTailFixedUs
+    const int64_t ksteps = shared_ksteps(gp, stage);
+    int64_t span = 0, units = 0;
+    if (ksteps) {
+        NsArgs na{};
+        int64_t cnt[8];
+        for (int x = 0; x < 8; ++x) cnt[x] = deal.cnt[x];
+        units = tail_split(cnt, ksteps, &na);
+        for (int x = 0; x < 8; ++x) {
+            const int64_t q = cnt[x] / kCusPerXcd, r = cnt[x] % kCusPerXcd;
+            const int64_t last = (units > 0 && na.xtail[x] > 0) ? (ksteps / 8 + na.xsplit[x] - 1) / na.xsplit[x] * 8
+                                                                : (r > 0 ? ksteps : 0);
+            span = std::max(span, q * ksteps + last);
+        }
+    } else {
+        std::vector<int64_t> ks[8];
+        xcd_seqs(gp, stage, deal, ks);
+        int64_t longest = 0;
+        units = head_split(ks, nullptr, &longest);
+        if (longest > 0) {
+            span = longest * 8;
+        } else {
+            for (int x = 0; x < 8; ++x) {
+                int64_t free_at[kCusPerXcd] = {0};
+                for (const int64_t k : ks[x]) {
+                    int64_t* cu = std::min_element(free_at, free_at + kCusPerXcd);
+                    *cu += k * 8;
+                    span = std::max(span, *cu);
+                }
+            }
+        }
+    }
+    return span * kStep + (units > 0 ? units * kUnit + kFixed : 0);
+}
+
+// The deal of a stage: on small tiles (no split) the balanced one; on big tiles the
+// balanced one when its modelled time is below the plain deal's. Balancing alone can
+// lose: 16 [2048, 2048] matrices go from 64 or 80 tiles per XCD (the 80 split in two
+// chunks) to 72 everywhere, whose last round of 8 short tiles does not pay for a split.
+XcdDeal stage_deal(const GroupPlan& gp, int stage, int64_t tile) {
+    const XcdDeal bal = xcd_deal(gp, stage, tile, true);
+    if (tile != kGemmBigM) return bal;
+    bool rotated = false;
+    for (size_t g = 0; g < gp.mats.size(); ++g) rotated = rotated || bal.rot[g] != 0;
+    if (!rotated) return bal;
+    const XcdDeal plain = xcd_deal(gp, stage, tile, false);
+    return deal_cost(gp, stage, bal) < deal_cost(gp, stage, plain) ? bal : plain;
+}
+
+// The split of a stage on big tiles under its deal: the tail split when its matrices
+// share K, else the head split (with mixed K the last tiles of an XCD are its shortest
+// ones and splitting them was measured to cost more than it saves). *head (optional)
+// tells which.
 int64_t split_plan(const GroupPlan& gp, int stage, NsArgs* na, bool* head = nullptr) {
-    int64_t cnt[8];
-    const int64_t ks = xcd_counts(gp, stage, cnt);
-    if (head) *head = ks == 0;
-    return ks ? tail_split(cnt, ks, na) : head_split(gp, stage, na);
+    const XcdDeal deal = stage_deal(gp, stage, kGemmBigM);
+    const int64_t ksteps = shared_ksteps(gp, stage);
+    if (head) *head = ksteps == 0;
+    if (ksteps) {
+        int64_t cnt[8];
+        for (int x = 0; x < 8; ++x) cnt[x] = deal.cnt[x];
+        return tail_split(cnt, ksteps, na);
+    }
+    std::vector<int64_t> ks[8];
+    xcd_seqs(gp, stage, deal, ks);
+    return head_split(ks, na);
 }
 
 // Big tiles of a stage, the first test of choose_tile.
@@ -257,17 +369,9 @@ GemmTile choose_tile(const GroupPlan& gp, bool sym, int stage) {
         same_n = same_n && gp.mats[k].n_p == gp.mats[0].n_p;
     }
     if (!((sym && stage == kStageGram) ? same_n : same_m)) return kTileSmall;
-    int64_t cb[8] = {0}, cs[8] = {0};
-    for (int k = 0; k < ng; ++k) {
-        const int64_t tb = gp.mats[k].m_p / kGemmBigM, ts = gp.mats[k].m_p / kGemmSmall;
-        const int64_t Tb = sym ? tb * (tb + 1) / 2 : tb * (gp.mats[k].n_p / kGemmBigN);
-        const int64_t Ts = sym ? ts * (ts + 1) / 2 : ts * (gp.mats[k].n_p / kGemmSmall);
-        for (int x = 0; x < 8; ++x) {
-            cb[x] += ((x + 1) * Tb >> 3) - (x * Tb >> 3);
-            cs[x] += ((x + 1) * Ts >> 3) - (x * Ts >> 3);
-        }
-    }
-    const int64_t mb = *std::max_element(cb, cb + 8), ms = *std::max_element(cs, cs + 8);
+    const int st = sym ? stage : int(kStageApply);
+    const XcdDeal db = stage_deal(gp, st, kGemmBigM), ds = stage_deal(gp, st, kGemmSmall);
+    const int64_t mb = *std::max_element(db.cnt, db.cnt + 8), ms = *std::max_element(ds.cnt, ds.cnt + 8);
     const int64_t rounds_big = (mb + kCusPerXcd - 1) / kCusPerXcd;
     const int64_t rounds_small = (ms + 2 * kCusPerXcd - 1) / (2 * kCusPerXcd);
     return (mb > 0 && rounds_big < rounds_small) ? kTileBig : kTileSmall;
@@ -530,28 +634,22 @@ GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym, char* ws = nullpt
             na.d[k].ntiles = int32_t((p.m_p / bm) * (p.n_p / bn));
         }
     }
-    // the kernels deal each matrix's tiles over the 8 XCDs in contiguous eighths
+    // the kernels deal each matrix's tiles over the 8 XCDs in rotated contiguous eighths
+    const XcdDeal deal = stage_deal(gp, sym ? stage : int(kStageApply), bm);
     int64_t per_xcd_max = 0;
-    for (int x = 0; x < 8; ++x) {
-        int64_t c = 0;
-        for (int k = 0; k < ng; ++k) {
-            const int64_t T = na.d[k].ntiles;
-            c += ((x + 1) * T >> 3) - (x * T >> 3);
-        }
-        per_xcd_max = std::max(per_xcd_max, c);
-    }
+    for (int k = 0; k < ng; ++k) na.d[k].rot = deal.rot[k];
+    for (int x = 0; x < 8; ++x) per_xcd_max = std::max(per_xcd_max, deal.cnt[x]);
     const int64_t tot = 8 * per_xcd_max;
     na.total = int32_t(tot);
     na.tail = nullptr;
     na.fix_total = 0;
     if (tile == kTileBig && (ws != nullptr || describe) && gp.tail_units > 0) {
-        int64_t cnt[8], fix = 0, longest = 0;
-        xcd_counts(gp, stage, cnt);
+        int64_t fix = 0, longest = 0;
         const int64_t units = split_plan(gp, stage, &na, head);
         if (units > 0 && units <= gp.tail_units) {
             for (int x = 0; x < 8; ++x) {
                 fix += na.xtail[x];
-                longest = std::max<int64_t>(longest, cnt[x] + int64_t(na.xtail[x]) * (na.xsplit[x] - 1));
+                longest = std::max<int64_t>(longest, deal.cnt[x] + int64_t(na.xtail[x]) * (na.xsplit[x] - 1));
             }
             na.tail = ws ? reinterpret_cast<float*>(ws + gp.tail) : nullptr;
             na.fix_total = int32_t(fix);
@@ -559,6 +657,23 @@ GemmTile plan_tiles(const GroupPlan& gp, NsArgs& na, bool sym, char* ws = nullpt
         }
     }
     return tile;
+}
+
+// Copies a planned stage's tiling (tile counts, XCD rotations, grid, split) into the
+// launch arguments.
+void take_tiling(NsArgs& na, const NsArgs& plan, int ng) {
+    for (int k = 0; k < ng; ++k) {
+        na.d[k].tiles = plan.d[k].tiles;
+        na.d[k].ntiles = plan.d[k].ntiles;
+        na.d[k].rot = plan.d[k].rot;
+    }
+    na.total = plan.total;
+    na.tail = plan.tail;
+    na.fix_total = plan.fix_total;
+    std::memcpy(na.xfull, plan.xfull, sizeof(na.xfull));
+    std::memcpy(na.xtail, plan.xtail, sizeof(na.xtail));
+    std::memcpy(na.xsplit, plan.xsplit, sizeof(na.xsplit));
+    std::memcpy(na.xpbase, plan.xpbase, sizeof(na.xpbase));
 }
 
 int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_hparams& hp,
@@ -619,6 +734,12 @@ int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_h
     na.cb = hp.ns_b;
     na.cc = hp.ns_c;
     na.decay = 1.0f - hp.lr * hp.weight_decay;
+    // the stages' tilings, the same in every iteration
+    NsArgs plan_gram{}, plan_poly{}, plan_apply{}, plan_final{};
+    const GemmTile sym_tile = plan_tiles(gp, plan_gram, true, ws, kStageGram);
+    const GemmTile poly_tile = plan_tiles(gp, plan_poly, true, ws, kStagePoly);
+    const GemmTile apply_tile = plan_tiles(gp, plan_apply, false, ws, kStageApply);
+    plan_tiles(gp, plan_final, false, nullptr, kStageApply);  // the last Apply keeps every tile whole
     for (int it = 0; it < hp.ns_steps; ++it) {
         const int cur = it & 1, nxt = cur ^ 1;
         const bool last = it + 1 == hp.ns_steps;
@@ -642,14 +763,13 @@ int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_h
             d.tall = p.tall ? 1 : 0;
             d.upd_coef = float(double(hp.lr) * dir_scale(hp, p.n));
         }
-        const GemmTile sym_tile = plan_tiles(gp, na, true, ws, kStageGram);
+        take_tiling(na, plan_gram, ng);
         rc = run_kernel(MUON_KCLASS_GRAM, s, "gram", [&] { return launch_ns_gemm(kModeGram, sym_tile, na, s); });
         if (rc) return rc;
-        const GemmTile poly_tile = plan_tiles(gp, na, true, ws, kStagePoly);
+        take_tiling(na, plan_poly, ng);
         rc = run_kernel(MUON_KCLASS_POLY, s, "poly", [&] { return launch_ns_gemm(kModePoly, poly_tile, na, s); });
         if (rc) return rc;
-        // the last Apply (fused update or fp32 O) keeps every tile whole
-        const GemmTile apply_tile = plan_tiles(gp, na, false, last ? nullptr : ws, kStageApply);
+        take_tiling(na, last ? plan_final : plan_apply, ng);
         const GemmMode mode = !last ? kModeApply : ((update_w && !eq6) ? kModeFinalW : kModeFinalO);
         rc = run_kernel(last ? MUON_KCLASS_APPLY_FINAL : MUON_KCLASS_APPLY, s, "apply",
                         [&] { return launch_ns_gemm(mode, apply_tile, na, s); });

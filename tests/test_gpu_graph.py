@@ -43,11 +43,12 @@ def make_state(torch, dev, shapes, key):
 
 
 # the last set runs its Gram, polynomial and Apply stages with split tail tiles and
-# their fixup launches (ten [2560, 2560] matrices: XCDs with 70 upper tiles split 6 in
-# 5 chunks, XCDs with 130 Apply tiles split 2 in 8)
+# their fixup launches (six [2560, 2560] matrices: the Gram and polynomial split the
+# last 9 or 10 of each XCD's 41 or 42 upper tiles in 3 chunks, the Apply the last 11 of
+# 75 in 2)
 @pytest.mark.parametrize("shapes", [[(128, 512)],
                                     [(768, 256), (256, 256), (1024, 256), (256, 1024), (1536, 256)],
-                                    [(2560, 2560)] * 10])
+                                    [(2560, 2560)] * 6])
 def test_captured_periodic_cycle_replays_bitwise(torch_dev, shapes):
     torch, dev = torch_dev
     hp = B.default_hparams(period_k=3)

@@ -11,8 +11,9 @@ Four sets exercise it:
     7 hold 80 tiles and split their last 16 (from matrices 12 to 15) in 2 chunks; the
     Apply (128 tiles per XCD) does not split;
   * 10 x [2560, 2560] (550 upper tiles): in the Gram and polynomial, XCDs 1 to 7 hold
-    70 tiles and split their last 6 (all from matrix 9) in 5 chunks; in the Apply,
-    XCDs 1, 3, 5 and 7 hold 130 tiles and split their last 2 (matrix 9) in 8 chunks;
+    70 tiles and split their last 6 (all from matrix 9) in 5 chunks (the plain deal: the
+    balanced one, 68 or 69 tiles everywhere, models slower); the Apply's balanced deal
+    gives every XCD 125 tiles, whose last round of 29 does not split;
   * [2048, 8448] and [8448, 2048]: the Gram and polynomial run on 128-wide tiles (72
     big upper tiles, one round either way), so the Apply also writes the row-major X'_r; every XCD holds 66
     Apply tiles and splits its last 2 (from the second matrix) in 8 chunks;
@@ -21,12 +22,14 @@ Four sets exercise it:
     256-wide tiles and every XCD splits its last 2 (from the second matrix) in 8
     chunks; the Apply (64 tiles per XCD) does not split.
 When the group's matrices differ in K and every XCD's tiles fit one round, the XCD
-instead runs its first (longest) tiles as K chunks, the head split. Two sets exercise it:
-  * [2048, 8192] and 3 x [2048, 2048] (144 upper tiles; K 32 and 8 units of 256): every
+instead runs its first (longest) tiles as K chunks, the head split. Three sets exercise it:
+  * [2048, 8192] and 4 x [2048, 2048] (180 upper tiles; K 32 and 8 units of 256): every
     XCD runs its 4 or 5 tiles of the first matrix as 3 chunks of 10 to 11 units (uneven
     chunks), its longest block 32 -> 11 units;
   * [6144, 3072] and [3072, 3072] (156 upper tiles; K 24 and 12 units): XCDs run their 9
-    or 10 tiles of the first matrix as 2 chunks, 24 -> 12 units.
+    or 10 tiles of the first matrix as 2 chunks, 24 -> 12 units;
+  * [9216, 1536] and 6 x [1536, 1536] (147 upper tiles; K 36 and 6 units): XCDs run
+    their 2 or 3 tiles of the first matrix as 5 chunks of 7 to 8 units.
 The matrices with split tiles and the first one are checked against the float64
 oracle's Newton-Schulz at the bf16 tolerance, and each call is repeated to check
 that the fixed-order chunk sums make it bitwise repeatable. The library's plan
@@ -52,7 +55,7 @@ pytestmark = pytest.mark.gpu
 # (tail tiles, chunks)), split of the Apply
 CASES = [
     ([(2048, 2048)] * 16, [0, 12, 13, 14, 15], {1: (16, 2), 3: (16, 2), 5: (16, 2), 7: (16, 2)}, {}),
-    ([(2560, 2560)] * 10, [0, 9], {x: (6, 5) for x in range(1, 8)}, {1: (2, 8), 3: (2, 8), 5: (2, 8), 7: (2, 8)}),
+    ([(2560, 2560)] * 10, [0, 9], {x: (6, 5) for x in range(1, 8)}, {}),
     ([(2048, 8448), (8448, 2048)], [0, 1], {}, {x: (2, 8) for x in range(8)}),
     ([(4096, 4096)] * 2, [1], {x: (2, 8) for x in range(8)}, {}),
 ]
@@ -95,8 +98,9 @@ def test_split_tail_tiles_vs_oracle_and_repeatable(torch_dev, case):
 
 
 HEAD_CASES = [
-    ([(2048, 8192)] + [(2048, 2048)] * 3, [0, 3], {x: (-4 - (x & 1), 3) for x in range(8)}),
+    ([(2048, 8192)] + [(2048, 2048)] * 4, [0, 4], {x: (-4 - (x & 1), 3) for x in range(8)}),
     ([(6144, 3072), (3072, 3072)], [0, 1], {x: (-9 if x in (0, 4) else -10, 2) for x in range(8)}),
+    ([(9216, 1536)] + [(1536, 1536)] * 6, [0, 6], {x: (-2 if x in (0, 2, 5) else -3, 5) for x in range(8)}),
 ]
 
 

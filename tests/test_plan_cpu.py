@@ -8,7 +8,16 @@ library's C++:
     groups of at most 16;
   * tiles: the Gram and polynomial count the upper triangle of a [m, m] tile grid
     (diagonal included), the Apply every tile of [m, n]; each of the 8 XCDs takes a
-    contiguous eighth of every matrix's tiles;
+    contiguous eighth of every matrix's tiles, XCD x eighth (x + r) mod 8. In the
+    balanced deal each matrix in group order takes the r in 0..7 that leaves the XCDs'
+    loads (tiles times K / 256, K = n for the Gram and m otherwise) with the smallest
+    sum of squares, the smallest r on a tie; in the plain deal r = 0. 128-wide tiles
+    take the balanced deal; 256-wide tiles take it only when its modelled cost is lower:
+    the busiest XCD's span in K steps (q full rounds of K plus the last round's tiles or
+    their largest chunk under the split rules below; the longest block when a stage
+    with mixed K fits one round; otherwise a list schedule of the XCD's tiles, in order,
+    on 32 compute units) times 0.86 us, plus 0.13 us per partial tile and 10 us when the
+    stage splits;
   * tile width per stage: 256 when the stage has at least 512 such tiles (128 for the
     Gram); otherwise,
     when every matrix of the group has the same K for the stage (n for the Gram, m for
@@ -32,6 +41,7 @@ library's C++:
 Sets: the benchmark workloads, the GPU tests' sets, and a seeded sweep of random sets.
 """
 import ctypes
+import heapq
 import os
 
 import numpy as np
@@ -57,13 +67,24 @@ def eighths(total):
     return [((x + 1) * total >> 3) - (x * total >> 3) for x in range(XCDS)]
 
 
-def per_xcd(mats, stage, width):
-    cnt = [0] * XCDS
+def rotated_deal(mats, stage, width, balance):
+    """Per XCD, the K (units of 256) of each tile it takes, in order: XCD x takes eighth
+    (x + r) mod 8 of each matrix, r = 0 or, balanced, the r that leaves the XCDs' loads
+    (tiles times K) with the smallest sum of squares (the smallest r on a tie)."""
+    seqs = [[] for _ in range(XCDS)]
+    load = [0] * XCDS
     for m, n in mats:
         t = m // width
         total = t * (n // width) if stage == "apply" else t * (t + 1) // 2
-        cnt = [c + e for c, e in zip(cnt, eighths(total))]
-    return cnt
+        k = (n if stage == "gram" else m) // 256
+        e = eighths(total)
+        r = 0
+        if balance:
+            r = min(range(XCDS), key=lambda r: (sum((load[x] + e[(x + r) % XCDS] * k) ** 2 for x in range(XCDS)), r))
+        for x in range(XCDS):
+            seqs[x] += [k] * e[(x + r) % XCDS]
+            load[x] += e[(x + r) % XCDS] * k
+    return seqs
 
 
 def shared_k(mats, stage):
@@ -71,24 +92,10 @@ def shared_k(mats, stage):
     return ks.pop() if len(ks) == 1 else None
 
 
-def tile_width(mats, stage):
-    big = per_xcd(mats, stage, 256)
-    if sum(big) >= (128 if stage == "gram" else 512):
-        return 256
-    if shared_k(mats, stage) is None:
-        return 128
-    small = per_xcd(mats, stage, 128)
-    return 256 if max(big) > 0 and ceil_div(max(big), CUS) < ceil_div(max(small), 2 * CUS) else 128
-
-
-def tail_split(mats, stage):
-    """(partial tiles, {XCD: (tail tiles, chunks)}) of a stage on 256-wide tiles."""
-    k = shared_k(mats, stage)
-    if k is None:
-        return 0, {}
-    ksteps = k // 32
+def tail_split_of(counts, ksteps):
+    """(partial tiles, {XCD: (tail tiles, chunks)}) for per-XCD tile counts of one K."""
     out = {}
-    for x, c in enumerate(per_xcd(mats, stage, 256)):
+    for x, c in enumerate(counts):
         r = c % CUS
         if 0 < r <= CUS // 2:
             s = min(8, CUS // r, ksteps // 8)
@@ -103,15 +110,11 @@ def tail_split(mats, stage):
     return units, out
 
 
-def head_split(mats, stage):
-    """(partial tiles, {XCD: (-h, chunks)}) of a one-round stage with mixed K."""
-    seqs = [[] for _ in range(XCDS)]
-    for m, n in mats:
-        k = (n if stage == "gram" else m) // 256
-        for x, c in enumerate(per_xcd([(m, n)], stage, 256)):
-            seqs[x] += [k] * c
+def head_split_of(seqs):
+    """(partial tiles, {XCD: (-h, chunks)}, longest block in units of 256 or None when
+    the tiles do not fit one round)."""
     if max(len(v) for v in seqs) > CUS:
-        return 0, {}
+        return 0, {}, None
 
     def options(v):
         # (longest block, partial tiles, S, h) of every allowed split, and no split
@@ -132,12 +135,80 @@ def head_split(mats, stage):
         out[x] = (-h, S)
     units = sum(-h * S for h, S in out.values())
     if not out or (before - target) * 8 * 0.86 <= units * 0.13 + 10.0:
-        return 0, {}
-    return units, out
+        return 0, {}, before
+    return units, out, target
+
+
+def list_schedule(durations):
+    """Finish time of blocks taken in order, each by the first free of CUS units."""
+    free = [0] * CUS
+    heapq.heapify(free)
+    end = 0
+    for d in durations:
+        t = heapq.heappop(free) + d
+        end = max(end, t)
+        heapq.heappush(free, t)
+    return end
+
+
+def modelled_cost(seqs, k):
+    """Busiest XCD's span in K steps times 86 plus 13 per partial tile plus 1000 when the
+    stage splits (hundredths of a microsecond)."""
+    if k is not None:
+        ksteps = k // 32
+        units, split = tail_split_of([len(v) for v in seqs], ksteps)
+        span = 0
+        for x, v in enumerate(seqs):
+            q, r = divmod(len(v), CUS)
+            if x in split:
+                last = ceil_div(ksteps // 8, split[x][1]) * 8
+            else:
+                last = ksteps if r else 0
+            span = max(span, q * ksteps + last)
+    else:
+        units, split, longest = head_split_of(seqs)
+        if longest is not None:
+            span = longest * 8
+        else:
+            span = max(list_schedule([8 * kk for kk in v]) for v in seqs)
+    return span * 86 + (units * 13 + 1000 if units else 0)
+
+
+def deal(mats, stage, width):
+    """The deal a stage uses: balanced, except on 256-wide tiles when the plain deal's
+    modelled cost is not above the balanced one's (the plain deal when both are equal)."""
+    bal = rotated_deal(mats, stage, width, True)
+    if width != 256:
+        return bal
+    plain = rotated_deal(mats, stage, width, False)
+    if plain == bal:
+        return bal
+    k = shared_k(mats, stage)
+    return bal if modelled_cost(bal, k) < modelled_cost(plain, k) else plain
+
+
+def per_xcd(mats, stage, width):
+    return [len(v) for v in deal(mats, stage, width)]
+
+
+def tile_width(mats, stage):
+    big = per_xcd(mats, stage, 256)
+    if sum(big) >= (128 if stage == "gram" else 512):
+        return 256
+    if shared_k(mats, stage) is None:
+        return 128
+    small = per_xcd(mats, stage, 128)
+    return 256 if max(big) > 0 and ceil_div(max(big), CUS) < ceil_div(max(small), 2 * CUS) else 128
 
 
 def split_of(mats, stage):
-    return tail_split(mats, stage) if shared_k(mats, stage) is not None else head_split(mats, stage)
+    """(partial tiles, {XCD: (tiles, chunks)}) of a stage on 256-wide tiles."""
+    seqs = deal(mats, stage, 256)
+    k = shared_k(mats, stage)
+    if k is not None:
+        return tail_split_of([len(v) for v in seqs], k // 32)
+    units, split, _ = head_split_of(seqs)
+    return units, split
 
 
 def expected_plan(shapes):
@@ -185,6 +256,7 @@ def test_plan_of_random_sets():
     rng = np.random.default_rng(20240607)
     sizes = [1, 100, 128, 255, 256, 257, 512, 1000, 1536, 2048, 2304, 2560, 3072, 3840, 4096, 5120, 6144, 8192]
     splits = 0
+    chosen = {True: 0, False: 0}
     for trial in range(300):
         kinds = int(rng.integers(1, 4))
         pool = [(int(rng.choice(sizes)), int(rng.choice(sizes))) for _ in range(kinds)]
@@ -192,7 +264,14 @@ def test_plan_of_random_sets():
         want = expected_plan(shapes)
         assert B.ns5_plan(shapes) == want, (trial, shapes)
         splits += sum(1 for g in want for st in ("gram", "poly", "apply") if g[st][1])
+        for g in want:
+            mats = [(ceil_div(min(shapes[i]), PAD) * PAD, ceil_div(max(shapes[i]), PAD) * PAD) for i in g["indices"]]
+            for st in ("gram", "poly", "apply"):
+                bal = rotated_deal(mats, st, 256, True)
+                if bal != rotated_deal(mats, st, 256, False):
+                    chosen[deal(mats, st, 256) == bal] += 1
     assert splits > 20  # the sweep exercises the split rule, not only the tile rule
+    assert min(chosen.values()) > 50  # and both outcomes of the deal choice
 
 
 def test_plan_of_random_mixed_k_sets():
