@@ -207,16 +207,16 @@ int rownorm_update(const muon_matrix* mats, int32_t count, const muon_hparams* h
  * no timing events.
  * Limit: the RowNorm workspace of the matrices must fit the array. Per group of up to
  * 16 matrices (the same grouping as muon_step) it is the sum over the group of
- *   tall [A, B] (A > B):  4 B (ceil(A / 256) + 2) bytes,
+ *   tall [A, B] (A > B):  4 B (ceil(A / 64) + 2) bytes,
  *   flat [A, B]:          4 A bytes,
- * each part rounded up to 256 bytes; sixteen [30720, 5120] matrices take 40 MB. Beyond
+ * each part rounded up to 256 bytes; sixteen [30720, 5120] matrices take 158 MB. Beyond
  * it the call returns MUON_ERR_WORKSPACE and nothing runs.
  * Every call on one GPU uses that GPU's single array: calls that overlap in time on one
  * GPU (other streams, other threads) race and corrupt each other's results; serialise
  * them. The array keeps the last call's contents; no part of it needs to start at zero.
  * Errors: as rownorm_update (WORKSPACE for the limit), HIP when the current device or the
  * array's address cannot be looked up. */
-#define MUON_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define MUON_NOALLOC_SCRATCH_BYTES ((size_t)160 << 20)
 int rownorm_update_noalloc(const muon_matrix* mats, int32_t count, const muon_hparams* hp,
                            float* update_rms, void* stream);
 

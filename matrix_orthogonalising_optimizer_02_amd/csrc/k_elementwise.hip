@@ -307,8 +307,8 @@ __global__ __launch_bounds__(256) void k_colnorm_partial(ColArgs args) {
     const float mu = args.mu;
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
     if (VEC && c0 + 3 < d.cols) {
-        // rows in batches of kB, loads ahead of stores (16: each wave's 64 rows of the
-        // chunk in one batch; measured 0.6-1% faster than 8, 4 slower)
+        // rows in batches of kB, loads ahead of stores (16: each wave's 16 rows of the
+        // 64-row chunk in one batch)
         constexpr int kB = 16;
         for (int rb = r0 + wave; rb < r1; rb += 4 * kB) {
             floatx4 mv[kB], gv[kB];
@@ -362,15 +362,36 @@ __global__ __launch_bounds__(256) void k_colnorm_partial(ColArgs args) {
         d.partial[(int64_t)chunk * d.cols + c] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
 }
 
+// One block per kColFinCols columns of a matrix: wave w adds the column's chunk partials
+// of chunks [w q, (w + 1) q), q = ceil(chunks / 4), in chunk order (loads eight chunks
+// ahead); the four wave sums are then added as (s0 + s1) + (s2 + s3). The order is
+// fixed, so the norms are repeatable, and a single chunk's sum passes through exactly.
 __global__ __launch_bounds__(256) void k_colnorm_finalize(ColArgs args) {
+    static_assert(kColFinCols == 64, "one wave-wide column strip per block");
+    __shared__ float red[4][kColFinCols];
     const int t = blockIdx.x;
     int gi = 0;
     while (gi + 1 < args.n && t >= args.d[gi + 1].fin_begin) ++gi;
     const ColDesc& d = args.d[gi];
-    const int c = (t - d.fin_begin) * 256 + threadIdx.x;
-    if (c >= d.cols) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = (t - d.fin_begin) * kColFinCols + lane;
+    const int q = (d.chunks + 3) >> 2, k0 = wave * q, k1 = min(k0 + q, d.chunks);
     float s = 0.f;
-    for (int k = 0; k < d.chunks; ++k) s += d.partial[(int64_t)k * d.cols + c];
+    if (c < d.cols) {
+        int k = k0;
+        for (; k + 8 <= k1; k += 8) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = d.partial[(int64_t)(k + j) * d.cols + c];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s += v[j];
+        }
+        for (; k < k1; ++k) s += d.partial[(int64_t)k * d.cols + c];
+    }
+    red[wave][lane] = s;
+    __syncthreads();
+    if (wave != 0 || c >= d.cols) return;
+    s = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
     if (args.sums_only) {  // a row block's share of a sharded matrix: the caller reduces
         d.inv[c] = s;
         return;

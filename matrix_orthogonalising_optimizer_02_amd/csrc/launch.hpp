@@ -129,7 +129,7 @@ struct ColDesc {
     int32_t chunks;        // ceil(rows / kColChunkRows)
     int32_t tiles_c;       // ceil(cols / 256)
     int32_t tile_begin;    // first block of this matrix in the launch
-    int32_t fin_begin;     // first block of this matrix in the finalize launch
+    int32_t fin_begin;     // first block of this matrix in the finalize launch (kColFinCols columns each)
     float coef;
     float* part;           // optional: [cols] sums of R^2 per column
 };
@@ -254,8 +254,14 @@ struct SpArgs {
     double* sigma_sq;      // optional output, descending per matrix (null = not wanted)
 };
 
-constexpr int kColChunkRows = 256;
+// Tall RowNorm blocks: kColChunkRows rows x kColTileCols columns, one partial row of
+// column sums per chunk. 64-row blocks that each load their rows in one batch stream at
+// 6.2 TB/s on MI355X against 5.5 TB/s for 256-row blocks that loop over four batches
+// (the same read-read-write pattern on a [30720, 5120] matrix).
+constexpr int kColChunkRows = 64;
 constexpr int kColTileCols = 256;
+// Columns per block of the finalize, which adds a column's chunk partials.
+constexpr int kColFinCols = 64;
 // Rows up to this length keep M' in registers (one 256-thread block per row).
 constexpr int kRowMaxRegisterCols = 32 * 1024;
 

@@ -864,7 +864,7 @@ int run_rownorm(const GroupPlan& gp, const muon_matrix* mats, const muon_hparams
             d.coef = coef;
             d.part = part;
             col_total += int64_t(d.chunks) * d.tiles_c;
-            fin_total += (p.cols + 255) / 256;
+            fin_total += (p.cols + kColFinCols - 1) / kColFinCols;
             col_vec = col_vec && (p.cols % 4 == 0);
         }
     }
@@ -1504,7 +1504,7 @@ MUON_API int rownorm_shard_colsq(const muon_shard* shards, int32_t count, const 
             d.tile_begin = int32_t(tiles);
             d.fin_begin = int32_t(fin);
             tiles += int64_t(d.chunks) * d.tiles_c;
-            fin += (sp.cols + 255) / 256;
+            fin += (sp.cols + kColFinCols - 1) / kColFinCols;
         }
         bool vec = true;
         for (const ShardPlan& sp : g) vec = vec && (sp.cols % 4 == 0);
@@ -1550,7 +1550,7 @@ MUON_API int rownorm_shard_apply(const muon_shard* shards, int32_t count, const 
             f.cols = int32_t(sp.cols);
             f.chunks = 1;
             f.fin_begin = int32_t(fin);
-            fin += (sp.cols + 255) / 256;
+            fin += (sp.cols + kColFinCols - 1) / kColFinCols;
             if (sp.rows == 0) continue;
             ColDesc& d = aa.d[aa.n++];
             d.m = t.m;

@@ -9,7 +9,7 @@ at the fp32 tolerance (1e-5 relative Frobenius; W also through the W = 0 probe, 
 W' is the update itself), and one block holding the whole matrix must reproduce
 rownorm_update bit for bit (the same sums in the same order).
 Cases: uneven blocks (including an empty block and blocks that are not multiples of
-the 256-row chunk), columns not a multiple of 4, more blocks than one launch group,
+the 64-row chunk), columns not a multiple of 4, more blocks than one launch group,
 and the hidden-size scale rule.
 """
 import sys

@@ -74,7 +74,7 @@ def test_noalloc_matches_rownorm_update_twice(torch_dev):
 
 def test_noalloc_full_size_15b_set(torch_dev):
     """The 15B-scale set's RowNorm step: six tall matrices up to [30720, 5120] in one
-    group (about 11 MB of scratch)."""
+    group (about 43 MB of scratch)."""
     torch, dev = torch_dev
     wl = WL.LAYER_SET_15B_H5120
     hp = B.default_hparams()
