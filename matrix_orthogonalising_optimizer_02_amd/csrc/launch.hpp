@@ -262,8 +262,11 @@ constexpr int kColChunkRows = 64;
 constexpr int kColTileCols = 256;
 // Columns per block of the finalize, which adds a column's chunk partials.
 constexpr int kColFinCols = 64;
-// Rows up to this length keep M' in registers (one 256-thread block per row).
+// Rows up to this length keep M' in registers (one 256-thread block per row; rows
+// longer than kRowWideCols whose length is a multiple of 4 take a 1024-thread block).
 constexpr int kRowMaxRegisterCols = 32 * 1024;
+constexpr int kRowWideCols = 8192;
+static_assert(kRowMaxRegisterCols <= 8 * 4 * 1024, "wide rows: at most 8 float4 per thread");
 
 // Launchers return hipSuccess or the launch error.
 hipError_t launch_cast(const CastArgs& a, hipStream_t s);
@@ -271,6 +274,7 @@ hipError_t launch_frob(const FrobArgs& a, hipStream_t s);
 enum GemmTile : int { kTileSmall = 0, kTileBig = 1 };
 hipError_t launch_ns_gemm(GemmMode mode, GemmTile tile, const NsArgs& a, hipStream_t s);
 hipError_t launch_rownorm_rows(const RowArgs& a, int max_cols, bool vec, hipStream_t s);
+hipError_t launch_rownorm_rows_wide(const RowArgs& a, int max_cols, hipStream_t s);
 hipError_t launch_colnorm_partial(const ColArgs& a, bool vec, hipStream_t s);
 hipError_t launch_colnorm_finalize(const ColArgs& a, int fin_total, hipStream_t s);
 hipError_t launch_colnorm_apply(const ColArgs& a, bool vec, hipStream_t s);

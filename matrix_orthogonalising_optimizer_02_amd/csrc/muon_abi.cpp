@@ -820,34 +820,41 @@ int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_h
 int run_rownorm(const GroupPlan& gp, const muon_matrix* mats, const muon_hparams& hp, char* ws,
                 float* update_rms, hipStream_t s) {
     const float decay = 1.0f - hp.lr * hp.weight_decay;
-    RowArgs ra{};
-    ra.mu = hp.mu;
-    ra.decay = decay;
-    ra.eps = hp.eps;
+    RowArgs ra{}, rw{};  // flat rows; wide flat rows (kRowWideCols < cols <= kRowMaxRegisterCols, cols % 4 == 0)
+    ra.mu = rw.mu = hp.mu;
+    ra.decay = rw.decay = decay;
+    ra.eps = rw.eps = hp.eps;
     ColArgs ca{};
     ca.mu = hp.mu;
     ca.decay = decay;
     ca.eps = hp.eps;
-    int64_t rows_total = 0, col_total = 0, fin_total = 0;
-    int max_cols = 0;
+    int64_t rows_total = 0, wide_total = 0, col_total = 0, fin_total = 0;
+    int max_cols = 0, max_wide = 0;
     bool row_vec = true, col_vec = true;
     for (const MatPlan& p : gp.mats) {
         const muon_matrix& t = mats[p.idx];
         const float coef = float(double(hp.lr) * double(hp.gamma) * dir_scale(hp, p.n));
         float* part = update_rms ? reinterpret_cast<float*>(ws + p.rpart_rn) : nullptr;
         if (!p.tall) {
-            RowDesc& d = ra.d[ra.n++];
+            const bool wide = p.cols > kRowWideCols && p.cols <= kRowMaxRegisterCols && p.cols % 4 == 0;
+            RowArgs& a = wide ? rw : ra;
+            int64_t& total = wide ? wide_total : rows_total;
+            RowDesc& d = a.d[a.n++];
             d.g = t.g;
             d.m = t.m;
             d.w = t.w;
             d.rows = int32_t(p.rows);
             d.cols = int32_t(p.cols);
-            d.row_begin = int32_t(rows_total);
+            d.row_begin = int32_t(total);
             d.coef = coef;
             d.part = part;
-            rows_total += p.rows;
-            max_cols = std::max<int>(max_cols, int(p.cols));
-            row_vec = row_vec && (p.cols % 4 == 0);
+            total += p.rows;
+            if (wide) {
+                max_wide = std::max<int>(max_wide, int(p.cols));
+            } else {
+                max_cols = std::max<int>(max_cols, int(p.cols));
+                row_vec = row_vec && (p.cols % 4 == 0);
+            }
         } else {
             ColDesc& d = ca.d[ca.n++];
             d.g = t.g;
@@ -869,6 +876,12 @@ int run_rownorm(const GroupPlan& gp, const muon_matrix* mats, const muon_hparams
         }
     }
     int rc = MUON_OK;
+    if (rw.n > 0) {
+        rw.total = int32_t(wide_total);
+        rc = run_kernel(MUON_KCLASS_ROWNORM_ROWS, s, "rownorm_rows_wide",
+                        [&] { return launch_rownorm_rows_wide(rw, max_wide, s); });
+        if (rc) return rc;
+    }
     if (ra.n > 0) {
         ra.total = int32_t(rows_total);
         rc = run_kernel(MUON_KCLASS_ROWNORM_ROWS, s, "rownorm_rows",

@@ -214,9 +214,12 @@ def test_vanilla_step_mixed_shapes_w0_probe(torch_dev):
 
 # -------------------------------------------------------------- RowNorm ----
 
+# flat rows up to 8192 floats take 256-thread blocks, longer ones up to 32768 (a multiple
+# of 4) 1024-thread blocks (9000, 20480, 24000, 32768 here), longer still the re-reading
+# kernel (40000)
 RN_SHAPES = [(128, 512), (512, 128), (256, 256), (33, 77), (77, 33), (1, 4096), (4096, 1),
              (3, 40000), (300, 2048), (2048, 300), (64, 20480), (20480, 64), (5, 1023), (1023, 5),
-             (700, 257)]
+             (700, 257), (11, 9000), (6, 24000), (9, 32768)]
 
 
 @pytest.mark.parametrize("entry", ["rownorm_update", "muon_step"])
