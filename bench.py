@@ -602,7 +602,7 @@ def measure_ceilings(pkg, torch, dev, reps, say):
     mfma_tflops = flops / (mfma_ms * 1e-3) / 1e12
     res = {"copy": {"gbs": round(copy_gbs, 1), "frac_of_spec": round(copy_gbs / PEAK_HBM_GBS, 4),
                     "bytes_per_call": 8 * n, "ms_per_call": round(copy_ms, 4),
-                    "kernel": "muon_ceiling_copy: 256 threads, 16 KiB per block, non-temporal"},
+                    "kernel": "muon_ceiling_copy: 256 threads, 32 KiB per block, non-temporal"},
            "mfma": {"tflops": round(mfma_tflops, 1), "frac_of_spec": round(mfma_tflops / PEAK_BF16_TFLOPS, 4),
                     "flops_per_call": flops, "ms_per_call": round(mfma_ms, 4),
                     "kernel": "muon_ceiling_mfma: 256 blocks x 4 waves, 16 independent 32x32x16 bf16 MFMA chains "

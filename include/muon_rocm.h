@@ -341,7 +341,7 @@ int svd_entropy(const float* const* w, const int64_t* rows, const int64_t* cols,
  * (HIP events on `stream`) on the same GPU; neither is part of the optimizer step.
  * muon_ceiling_copy: dst[i] = src[i] for n fp32 elements (DEVICE pointers, 16-byte
  *   aligned, not overlapping), streamed as the step's HBM-bound passes stream: 256
- *   threads, 16 KiB contiguous per block, all loads of a thread before its stores,
+ *   threads, 32 KiB contiguous per block, all loads of a thread before its stores,
  *   non-temporal hints. 8 n bytes of HBM traffic. Errors: INVALID_ARG, ALIGN, ALIAS,
  *   TOO_LARGE, HIP.
  * muon_ceiling_mfma: `blocks` blocks of four waves; every wave issues `iters` rounds of

@@ -12,10 +12,12 @@
 namespace muon {
 namespace {
 
-// Copy: 256 threads, kCopyVec float4 per thread, one contiguous 16 KiB chunk per block,
-// every load of a thread issued before its stores, non-temporal hints (the same access
-// pattern as the streaming passes of the step).
-constexpr int kCopyVec = 4;
+// Copy: 256 threads, kCopyVec float4 per thread, one contiguous 32 KiB chunk per block,
+// every load of a thread issued before its stores, non-temporal hints (the access
+// pattern of the streaming passes of the step). Of the variants measured on MI355X
+// (2, 4, 8 and 16 float4 per thread; 64 to 1024 threads; plain or non-temporal loads and
+// stores; a persistent grid) this one copies fastest, 6.36 TB/s on 1 GiB.
+constexpr int kCopyVec = 8;
 constexpr int64_t kCopyBlockElems = 256 * 4 * kCopyVec;
 
 __global__ __launch_bounds__(256) void k_ceiling_copy(const float* __restrict__ src, float* __restrict__ dst,
