@@ -27,6 +27,7 @@ struct CastDesc {
     int32_t rows, cols, rows_p, cols_p;
     int32_t tiles_c;       // cols_p / 64
     int32_t tile_begin;    // first tile of this matrix in the launch
+    int32_t wide;          // nonzero: no transposed copy; tiles of 16 rows x 256 columns
 };
 
 struct CastArgs {

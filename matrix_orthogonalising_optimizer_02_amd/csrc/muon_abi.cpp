@@ -709,6 +709,7 @@ int run_refresh(const GroupPlan& gp, const std::vector<IoPtrs>& io, const muon_h
         d.rows_p = int32_t(p.rows_p);
         d.cols_p = int32_t(p.cols_p);
         d.tiles_c = int32_t(p.cols_p / 64);
+        d.wide = d.transp == nullptr ? 1 : 0;  // cols_p is a multiple of 256
         d.tile_begin = int32_t(tiles);
         tiles += p.cast_tiles;
     }

@@ -130,6 +130,25 @@ def test_ns5_stages_on_big_tiles_by_rounds(torch_dev):
     log(f"  five [2304, 2304], matrix 4: rel err {err:.3e}, worst line {line:.3e}")
 
 
+def test_ns5_wide_cast_tiles_ragged_tall(torch_dev):
+    """Three [8450, 2046] matrices and one [8450, 2048]: 144 upper tiles of 256, so the
+    Gram reads X_c alone and the cast writes no transposed copy; it then takes its wide
+    16 x 256 tiles, here with ragged rows (8450 of 8704) and, for the first three,
+    columns that are not a multiple of 4 (2046: the element-wise path; the padded
+    columns of X_c must be zeros). The first and last matrix against the oracle."""
+    torch, dev = torch_dev
+    shapes = [(8450, 2046)] * 3 + [(8450, 2048)]
+    plan = B.ns5_plan(shapes)
+    assert len(plan) == 1 and plan[0]["gram"][0] == 256
+    xs = [gauss(111, i, s) for i, s in enumerate(shapes)]
+    log(f"ns5_batched: {shapes}")
+    outs = B.ns5_batched([to_dev(torch, dev, x) for x in xs])
+    torch.cuda.synchronize()
+    for i in (0, 3):
+        err, line = assert_ns_close(to_host(outs[i]), O.newton_schulz(xs[i]), shapes[i], i)
+        log(f"  matrix {i} {shapes[i]}: rel err {err:.3e}, worst line {line:.3e}")
+
+
 def test_ns5_in_place_zero_and_degenerate(torch_dev):
     torch, dev = torch_dev
     x = gauss(102, 0, (300, 200))
