@@ -184,12 +184,15 @@ def pick_workload(name):
 
 
 def cpu_baseline(wl, k):
-    """Time the float64 oracle on the workload's smallest matrix and scale to the set.
+    """Time the float64 oracle on a sample of the workload's matrices and scale to the set.
 
     Sample: the median of three refresh steps and of three RowNorm steps of the oracle
-    on one matrix (about 12 s of host work).
+    on the smallest matrix (about 11 s of host work), plus one refresh step on a second,
+    longer matrix of the set whose size is at most three times the first (about 10 s).
     The refresh time is scaled by the oracle's own flop count (Eq. 2 as written:
-    X X^T, A X and A (A X), 8 m^2 n per iteration) and the RowNorm time by elements.
+    X X^T, A X and A (A X), 8 m^2 n per iteration), at the sampled matrices' combined
+    seconds per flop; the RowNorm time by elements. The two matrices' seconds per flop
+    are reported, so the scaling can be checked.
     """
     import numpy as np
     from oracle import muon_oracle as O
@@ -200,11 +203,17 @@ def cpu_baseline(wl, k):
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    idx = min(range(len(wl.shapes)), key=lambda i: wl.shapes[i][0] * wl.shapes[i][1])
+    sizes = [s[0] * s[1] for s in wl.shapes]
+    idx = min(range(len(wl.shapes)), key=lambda i: sizes[i])
     shape = wl.shapes[idx]
-    w, m, g = WL.host_inputs(wl, idx)
     hp = O.OracleHParams(period_k=k)
-    reps = 3  # median of three: about 12 s of host work on the 5120 x 5120 matrix
+
+    def oflops(s):
+        mm, nn = min(s), max(s)
+        return hp.ns_steps * 8.0 * mm * mm * nn
+
+    w, m, g = WL.host_inputs(wl, idx)
+    reps = 3  # median of three: about 11 s of host work on the 5120 x 5120 matrix
     t_refs, t_rns = [], []
     for _ in range(reps):
         t0 = time.perf_counter()
@@ -214,19 +223,31 @@ def cpu_baseline(wl, k):
         O.rownorm_step(w, m, g, hp)
         t_rns.append(time.perf_counter() - t0)
     t_ref, t_rn = sorted(t_refs)[reps // 2], sorted(t_rns)[reps // 2]
-
-    def oflops(s):
-        mm, nn = min(s), max(s)
-        return hp.ns_steps * 8.0 * mm * mm * nn
-
-    ref_total = t_ref * sum(oflops(s) for s in wl.shapes) / oflops(shape)
+    # a second, longer matrix (the largest of at most three times the first one's size)
+    second = [i for i in range(len(wl.shapes)) if sizes[idx] < sizes[i] <= 3 * sizes[idx]]
+    rates = {f"{shape[0]}x{shape[1]}": t_ref / oflops(shape)}
+    t_sum, f_sum = t_ref, oflops(shape)
+    second_desc = "no second matrix of at most three times its size"
+    if second:
+        j = max(second, key=lambda i: sizes[i])
+        w2, m2, g2 = WL.host_inputs(wl, j)
+        t0 = time.perf_counter()
+        O.vanilla_step(w2, m2, g2, hp)
+        t2 = time.perf_counter() - t0
+        name2 = f"{wl.shapes[j][0]}x{wl.shapes[j][1]}"
+        rates[name2] = t2 / oflops(wl.shapes[j])
+        t_sum, f_sum = t_sum + t2, f_sum + oflops(wl.shapes[j])
+        second_desc = f"one refresh step ({t2:.1f} s) on the {name2} matrix"
+    ref_total = t_sum / f_sum * sum(oflops(s) for s in wl.shapes)
     rn_total = t_rn * wl.elements / (shape[0] * shape[1])
     avg_ms = 1e3 * (ref_total + (k - 1) * rn_total) / k
     return {"value": round(avg_ms, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
             "host": host_info(),
-            "sample": f"oracle refresh step ({t_ref:.1f} s) and RowNorm step ({t_rn:.2f} s), medians of "
-                      f"{reps} runs on the {shape[0]}x{shape[1]} matrix, scaled by flops and elements to the "
-                      f"{len(wl.shapes)}-matrix set; value = mean ms per optimizer step over a K={k} cycle",
+            "sample": f"oracle refresh step ({t_ref:.1f} s) and RowNorm step ({t_rn:.2f} s), medians of {reps} runs on "
+                      f"the {shape[0]}x{shape[1]} matrix, and {second_desc}; refresh scaled by the oracle's flops at the "
+                      f"sampled matrices' combined rate, RowNorm by elements, to the {len(wl.shapes)}-matrix set; "
+                      f"value = mean ms per optimizer step over a K={k} cycle",
+            "seconds_per_gflop": {kk: round(v * 1e9, 4) for kk, v in rates.items()},
             "vanilla_step_ms": round(1e3 * ref_total, 1), "rownorm_step_ms": round(1e3 * rn_total, 1)}
 
 
