@@ -37,7 +37,9 @@ that the fixed-order chunk sums make it bitwise repeatable. The library's plan
 it fails the test; the rule itself is checked on the CPU over many sets. A seeded
 sweep of six further sets (sides 2048 to 3072, one or two shapes, up to 16 matrices,
 kept when the plan splits a tail or takes 256-wide tiles below 512 of them) checks the
-first and last matrix of each against the oracle and every output for repeatability.
+first and last matrix of each against the oracle and every output for repeatability;
+a seeded sweep of four sets that take the head split (sides 1024 to 2048, some ragged,
+both orientations) does the same.
 """
 import sys
 
@@ -172,6 +174,48 @@ def test_random_big_sets_vs_oracle(torch_dev, case):
         assert torch.equal(o, o2), f"matrix {i}: two calls differ"
     checked = sorted({plan[0]["indices"][0], plan[-1]["indices"][-1]})
     for i in checked:
+        ref = O.newton_schulz(xs[i].astype(np.float32).astype(np.float64))
+        oh = outs[i].detach().cpu().numpy().astype(np.float64)
+        err, line = assert_ns_close(oh, ref, shapes[i], i)
+        log(f"  matrix {i} {shapes[i]}: rel err {err:.3e}, worst line {line:.3e}")
+
+
+def random_head_sets(count=4, seed=20241205):
+    """Seeded sets that take the head split: m from 1024 to 2048, two or three values of
+    n (1 to 4 times m, some ragged by 100), random orientation, 3 to 9 matrices; kept
+    when the Gram's plan splits the first tiles of some XCD."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        m = int(rng.choice([1024, 1536, 2048]))
+        ns = [int(rng.choice([1, 2, 3, 4])) * m + int(rng.choice([0, 0, 100])) for _ in range(int(rng.integers(2, 4)))]
+        shapes = []
+        for _ in range(int(rng.integers(3, 10))):
+            n = ns[int(rng.integers(0, len(ns)))]
+            shapes.append((m, n) if rng.random() < 0.5 else (n, m))
+        plan = B.ns5_plan(shapes)
+        if any(h < 0 for g in plan for h, _ in g["gram"][1].values()):
+            out.append(shapes)
+    return out
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_random_head_split_sets_vs_oracle(torch_dev, case):
+    """The head split on seeded sets with ragged sides and both orientations: every
+    output bitwise repeatable; the group's first matrix (whose tiles are the split ones)
+    and its last against the oracle."""
+    torch, dev = torch_dev
+    shapes = random_head_sets()[case]
+    plan = B.ns5_plan(shapes)
+    xs = [WL.host_normal(41 + case, WL.ROLE_G, i, s, 1e-3) for i, s in enumerate(shapes)]
+    ins = [torch.from_numpy(x.astype(np.float32)).to(dev) for x in xs]
+    log(f"ns5_batched: {shapes}, Gram {plan[0]['gram']}")
+    outs = B.ns5_batched(ins)
+    outs2 = B.ns5_batched(ins)
+    torch.cuda.synchronize()
+    for i, (o, o2) in enumerate(zip(outs, outs2)):
+        assert torch.equal(o, o2), f"matrix {i}: two calls differ"
+    for i in sorted({plan[0]["indices"][0], plan[-1]["indices"][-1]}):
         ref = O.newton_schulz(xs[i].astype(np.float32).astype(np.float64))
         oh = outs[i].detach().cpu().numpy().astype(np.float64)
         err, line = assert_ns_close(oh, ref, shapes[i], i)
