@@ -42,13 +42,15 @@ def make_state(torch, dev, shapes, key):
     return w, m, g
 
 
-# the last set runs its Gram, polynomial and Apply stages with split tail tiles and
+# the third set runs its Gram, polynomial and Apply stages with split tail tiles and
 # their fixup launches (six [2560, 2560] matrices: the Gram and polynomial split the
 # last 9 or 10 of each XCD's 41 or 42 upper tiles in 3 chunks, the Apply the last 11 of
-# 75 in 2)
+# 75 in 2); the last, [2048, 8192] and four [2048, 2048], runs its Gram with the head
+# split (each XCD's tiles of the first matrix in 3 chunks) and its fixup
 @pytest.mark.parametrize("shapes", [[(128, 512)],
                                     [(768, 256), (256, 256), (1024, 256), (256, 1024), (1536, 256)],
-                                    [(2560, 2560)] * 6])
+                                    [(2560, 2560)] * 6,
+                                    [(2048, 8192)] + [(2048, 2048)] * 4])
 def test_captured_periodic_cycle_replays_bitwise(torch_dev, shapes):
     torch, dev = torch_dev
     hp = B.default_hparams(period_k=3)
